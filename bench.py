@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-head windowed KV decode step on one MI355X.
+
+Workload (default): 48 layers x 8 KV heads (24 query heads, GQA group 3),
+head_dim 128, bf16, block_size 16, per-head windows drawn from
+{1024, 4096, 16384, 65536} with weights 0.2/0.3/0.3/0.2 (numpy seed 0),
+context 112K (114,688 tokens), batch 1.  One step = append of the new token
+for all 48 layers + decode attention (split + merge) over exactly the last
+w_h tokens of every head, one launch of each kernel for the whole stack.
+Inputs are synthetic N(0,1) K/V and N(0,1/128) q, resident in HBM before the
+timed region starts.
+
+Prints one JSON line.  Extra legs: `roofline` (the split kernel, timed with
+HIP events on its own stream), `cpu_baseline` (the fp64 CPU oracle on a
+bounded sample of the same step) and `per_layer_graph` (48 per-layer launch
+triplets captured in one HIP graph).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "decode tokens/s + effective KV-read GB/s (% of HBM peak), per-head-window attn"
+KV_BYTES_PER_TOK_HEAD = 512  # K + V row: 2 x 128 x bf16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "hwkv_internal.h"):
+        with open(os.path.join(ROOT, "head_windowed_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(split_launch_bytes: float):
+    """HBM traffic of one split launch from committed rocprofv3 counter runs,
+    valid only while the kernel source is the one the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "decode_split_stack48_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import head_windowed_kv_amd as H
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    n_layers, n_kv, G, d, bs = 48, 8, 3, 128, 16
+    L0 = synth.CTX_112K
+    n_seqs = 1
+    windows = synth.stack_windows(n_layers, n_kv, 0)
+    lay = H.hwkv_layout_create(windows, bs, d, torch.bfloat16, args.split_tokens)
+    desc = lay.desc()
+    cache = H.make_cache(lay, n_seqs, device=dev)
+    cap = int(((windows.astype(np.int64) + bs - 1) // bs * bs).max())
+    n_hist = min(L0, cap)
+
+    # ---- fill: per layer, the last n_hist positions before L0 ----
+    t_fill = time.time()
+    pos_hist = torch.full((n_seqs,), L0 - n_hist, dtype=torch.int64, device=dev)
+    for l in range(n_layers):
+        g = synth.gen(103 * 100003 + l, dev)
+        k = synth.randn((1, n_seqs, n_hist, n_kv, d), torch.bfloat16, g)
+        v = synth.randn((1, n_seqs, n_hist, n_kv, d), torch.bfloat16, g)
+        H.hwkv_append(cache, l, 1, pos_hist, k, v)
+        del k, v
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+
+    n_steps = args.warmup + args.steps
+    g = synth.gen(104, dev)
+    q = synth.randn((n_layers, n_seqs, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+    k_new = synth.randn((n_steps, n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
+    v_new = synth.randn((n_steps, n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
+    pos = [torch.full((n_seqs,), L0 + i, dtype=torch.int64, device=dev) for i in range(n_steps)]
+    ctx = [torch.full((n_seqs,), L0 + i + 1, dtype=torch.int64, device=dev)
+           for i in range(n_steps)]
+    ws = H.make_workspace(lay, 0, n_layers, n_seqs, n_kv * G, device=dev)
+    out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    # algorithmic K/V bytes of one decode step: every head reads min(w, L) rows
+    def step_bytes(L):
+        return float(np.minimum(windows.astype(np.int64), L).sum()) * KV_BYTES_PER_TOK_HEAD
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def run_step(i, evp=None):
+        H.hwkv_append(cache, 0, n_layers, pos[i], k_new[i], v_new[i], stream=stream)
+        if evp is not None:
+            evp[0].record(stream)
+        H.hwkv_decode_split(cache, 0, n_layers, ctx[i], q, scale, ws, stream=stream)
+        if evp is not None:
+            evp[1].record(stream)
+        H.hwkv_decode_merge(cache, 0, n_layers, ctx[i], ws, out, stream=stream)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for j in range(args.steps):
+        run_step(args.warmup + j, ev[j])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    split_ms = [a.elapsed_time(b) for a, b in ev]
+    split_avg_ms = sum(split_ms) / len(split_ms)
+    bytes_step = step_bytes(L0 + args.warmup + 1)
+    tok_per_s = n_seqs * args.steps / (total_ms / 1e3)
+    kv_gbps = bytes_step / (ms_per_step / 1e3) / 1e9
+    split_gbps = bytes_step / (split_avg_ms / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "stack48_ctx112k_decode_step",
+            "layers": n_layers, "kv_heads": n_kv, "q_heads": n_kv * G, "head_dim": d,
+            "block_size": bs, "context": L0, "batch": n_seqs,
+            "windows": "per (layer, head) from {1024,4096,16384,65536} p=.2/.3/.3/.2, "
+                       "numpy default_rng(0)",
+            "split_tokens": desc.split_tokens,
+            "launch": "one append + one split + one merge launch for all 48 layers",
+        },
+        "kv_read_bytes_per_step": bytes_step,
+        "kv_read_gbps": round(kv_gbps, 1),
+        "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_split_kernel<bf16, d128, G3>",
+            "achieved": round(split_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(bytes_step),
+            "avg_launch_ms": round(split_avg_ms, 4),
+            "algorithmic_bytes_per_launch": bytes_step,
+        },
+        "fill_seconds": round(t_fill, 2),
+    }
+
+    if not args.no_graph:
+        result["per_layer_graph"] = per_layer_graph(H, torch, cache, lay, windows, q, k_new,
+                                                    v_new, L0 + n_steps, n_seqs, n_kv, G, d,
+                                                    step_bytes)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(windows, L0, n_kv, G, d, args.cpu_seconds,
+                                              tok_per_s)
+    print(json.dumps(result), flush=True)
+
+
+def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n_kv, G, d,
+                    step_bytes):
+    """The model-realistic launch pattern: per layer append -> split -> merge
+    (each layer's q only exists after the previous layer), 144 launches
+    captured once in a HIP graph and replayed; positions live in device
+    scalars updated by a fill kernel outside the graph."""
+    dev = q.device
+    n_layers = windows.shape[0]
+    pos = torch.full((n_seqs,), L, dtype=torch.int64, device=dev)
+    ctx = torch.full((n_seqs,), L + 1, dtype=torch.int64, device=dev)
+    wss = [H.make_workspace(lay, l, 1, n_seqs, n_kv * G, device=dev) for l in range(n_layers)]
+    out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    kn = k_new[0].clone()
+    vn = v_new[0].clone()
+    qs = [q[l:l + 1].contiguous() for l in range(n_layers)]
+    kns = [kn[l:l + 1].contiguous() for l in range(n_layers)]
+    vns = [vn[l:l + 1].contiguous() for l in range(n_layers)]
+    outs = [out[l:l + 1] for l in range(n_layers)]
+    scale = 1.0 / math.sqrt(d)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for l in range(n_layers):  # warm the launch path once, eagerly
+            H.hwkv_append(cache, l, 1, pos, kns[l], vns[l])
+            H.hwkv_decode_attn(cache, l, 1, ctx, qs[l], scale, wss[l], outs[l])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for l in range(n_layers):
+                H.hwkv_append(cache, l, 1, pos, kns[l], vns[l])
+                H.hwkv_decode_attn(cache, l, 1, ctx, qs[l], scale, wss[l], outs[l])
+    torch.cuda.synchronize()
+    n_rep = 20
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(n_rep + 3):
+        pos.fill_(L + 1 + i)
+        ctx.fill_(L + 2 + i)
+        e0.record(s)
+        graph.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    b = step_bytes(L + 2)
+    return {"ms_per_step_median": round(ms, 4), "tokens_per_s": round(n_seqs / (ms / 1e3), 2),
+            "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
+            "launches_per_step": 3 * n_layers, "replays": n_rep}
+
+
+def cpu_baseline(windows, L, n_kv, G, d, target_s, gpu_tok_s):
+    """The fp64 oracle, as it is, on the host cores: one decode step of the
+    first few layers (bounded sample), scaled to the full 48-layer step by the
+    K/V bytes it reads."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    n_layers = windows.shape[0]
+    threads = oracle.threads()
+    spent = 0.0
+    bytes_done = 0.0
+    layers_done = 0
+    total_bytes = float(np.minimum(windows.astype(np.int64), L).sum()) * KV_BYTES_PER_TOK_HEAD
+    for l in range(n_layers):
+        W = int(windows[l].max())
+        g = synth.gen(9000 + l)
+        q = synth.randn((1, 1, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+        k = synth.randn((1, 1, W, n_kv, d), torch.bfloat16, g)
+        v = synth.randn((1, 1, W, n_kv, d), torch.bfloat16, g)
+        qr, kr, vr = synth.to_raw(q), synth.to_raw(k), synth.to_raw(v)
+        t = time.time()
+        oracle.decode(windows[l:l + 1], [L], qr, kr, vr, [L - W], 1.0 / math.sqrt(d))
+        spent += time.time() - t
+        bytes_done += float(np.minimum(windows[l].astype(np.int64), L).sum()) * \
+            KV_BYTES_PER_TOK_HEAD
+        layers_done += 1
+        if spent >= target_s:
+            break
+    step_s = spent * total_bytes / bytes_done
+    return {"value": round(1.0 / step_s, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "decode step of layers 0..%d of 48 (%.2f GB of K/V), %.1f s, scaled to the "
+                      "full step by bytes" % (layers_done - 1, bytes_done / 1e9, spent),
+            "kv_read_gbps": round(bytes_done / spent / 1e9, 3),
+            "gpu_over_cpu": round(gpu_tok_s * step_s, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,492 @@
+// Decode attention over exactly the last w_h resident tokens of every KV head
+// (HeadWiseKV write-up, 摘要: the policy is materialised as per-head
+// residency, not as a mask over a full cache; 核心技术 2: each head reads its
+// own block table of ceil(w_h / block_size) blocks).
+//
+// Stage 1 (split): one workgroup per (work item = (layer, kv head, split),
+// sequence).  A split is split_tokens consecutive positions of the window
+// [max(0, L-w), L); the workgroup streams the K/V rows of those positions
+// through the head's ring of blocks and keeps, for the G query heads of the
+// GQA group, an online-softmax state (running max m, sum l, weighted sum acc)
+// in registers.  Decode is HBM-bound (about 3 flop per byte read), so there
+// is no MFMA here: the design goal is to keep enough 128-bit loads in flight.
+//
+// Work layout inside a workgroup (256 threads = 4 wave64):
+//   - a wave processes one whole block (16 tokens x 256 B of K, same of V) at
+//     a time, blocks of the split interleaved over the 4 waves, two blocks in
+//     flight per wave;
+//   - the 64 lanes form 8 groups of 8; group g owns rows g and g+8 of the
+//     block, lane r of a group owns 16-byte chunks r and r+8 of each row, so
+//     every load instruction of the wave reads whole 128-byte lines;
+//   - q.k partial dots use v_dot2_f32_bf16 (bf16 products are exact in fp32)
+//     and are summed over the 8 lanes of a group with DPP;
+//   - each group keeps its own softmax state; states are merged across groups
+//     and waves once, at the end, in a fixed order (results do not depend on
+//     the batch composition or on timing).
+//
+// Stage 2 (merge): per (layer, sequence, kv head), combine the splits:
+//   M = max_s m_s;  o = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
+// Scores are kept in the log2 domain (s * scale * log2 e) so every
+// exponential is one v_exp_f32.
+#include <hip/hip_runtime.h>
+
+#include "hwkv_internal.h"
+
+namespace hwkv {
+namespace {
+
+constexpr int kBS = 16;  // block_size of every supported layout
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kEmptyMax = -1e30f;  // running max of a state that has seen no token
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16
+typedef float f32x4 __attribute__((ext_vector_type(4)));     // 4 fp32
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 lanes of a group; every lane of the group gets the sum.
+__device__ __forceinline__ float group8_sum(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: pairs
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: quads
+    x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+    return x;
+}
+
+// Lane i gets lane i^8 (rotate a 16-lane row by 8).
+__device__ __forceinline__ float xor8(float x) { return dpp<0x128>(x); }
+// Lane i gets lane i^16 (swizzle, bit mode: and 0x1f, xor 0x10).
+__device__ __forceinline__ float xor16(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Element type traits: a 16-byte chunk holds EPC elements.
+template <bool BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+    static constexpr int kBytes = 2;
+    typedef u32x4 Chunk;  // 8 bf16
+};
+template <>
+struct Elem<false> {
+    static constexpr int kBytes = 4;
+    typedef f32x4 Chunk;  // 4 fp32
+};
+
+template <bool BF16, int D, int G>
+struct SplitCfg {
+    static constexpr int EB = Elem<BF16>::kBytes;
+    static constexpr int ROW = D * EB;    // bytes per K (or V) row
+    static constexpr int NC = ROW / 128;  // 16-byte chunks per lane per row
+    static constexpr int EPC = 16 / EB;   // elements per chunk
+    static constexpr int DPL = NC * EPC;  // dims owned per lane
+    static constexpr int ROWS = kBS / 8;  // rows per group per block
+    static_assert(NC >= 1 && ROW % 128 == 0, "row must be a multiple of 128 bytes");
+};
+
+// partial dot product of one row chunk with one query chunk
+__device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k, float acc) {
+    acc = dot2_bf16(q.x, k.x, acc);
+    acc = dot2_bf16(q.y, k.y, acc);
+    acc = dot2_bf16(q.z, k.z, acc);
+    acc = dot2_bf16(q.w, k.w, acc);
+    return acc;
+}
+__device__ __forceinline__ float chunk_dot(const f32x4& q, const f32x4& k, float acc) {
+    acc = fmaf(q.x, k.x, acc);
+    acc = fmaf(q.y, k.y, acc);
+    acc = fmaf(q.z, k.z, acc);
+    acc = fmaf(q.w, k.w, acc);
+    return acc;
+}
+
+// widen element e of a chunk to fp32
+__device__ __forceinline__ float chunk_elem(const u32x4& v, int e) {
+    switch (e >> 1) {
+        case 0: return (e & 1) ? bf16_hi(v.x) : bf16_lo(v.x);
+        case 1: return (e & 1) ? bf16_hi(v.y) : bf16_lo(v.y);
+        case 2: return (e & 1) ? bf16_hi(v.z) : bf16_lo(v.z);
+        default: return (e & 1) ? bf16_hi(v.w) : bf16_lo(v.w);
+    }
+}
+__device__ __forceinline__ float chunk_elem(const f32x4& v, int e) {
+    switch (e) {
+        case 0: return v.x;
+        case 1: return v.y;
+        case 2: return v.z;
+        default: return v.w;
+    }
+}
+
+template <bool BF16, int D, int G>
+struct BlockRegs {
+    typedef typename Elem<BF16>::Chunk Chunk;
+    typedef SplitCfg<BF16, D, G> C;
+    Chunk k[C::ROWS][C::NC];
+    Chunk v[C::ROWS][C::NC];
+    bool valid[C::ROWS];
+};
+
+// Issue the loads of one block for this lane (rows g + 8*rho, chunks r + 8*c).
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void load_block(BlockRegs<BF16, D, G>& br, const uint8_t* blk,
+                                           bool blk_ok, int64_t lb, int64_t t0, int64_t t1,
+                                           int g, int r) {
+    typedef SplitCfg<BF16, D, G> C;
+    typedef typename Elem<BF16>::Chunk Chunk;
+#pragma unroll
+    for (int rho = 0; rho < C::ROWS; rho++) {
+        const int row = g + 8 * rho;
+        const int64_t pos = lb * kBS + row;
+        const bool ok = blk_ok && pos >= t0 && pos < t1;
+        br.valid[rho] = ok;
+        const uint8_t* krow = blk + row * C::ROW;
+        const uint8_t* vrow = krow + kBS * C::ROW;
+#pragma unroll
+        for (int c = 0; c < C::NC; c++) {
+            if (ok) {
+                br.k[rho][c] = __builtin_nontemporal_load(
+                    reinterpret_cast<const Chunk*>(krow + (c * 8 + r) * 16));
+                br.v[rho][c] = __builtin_nontemporal_load(
+                    reinterpret_cast<const Chunk*>(vrow + (c * 8 + r) * 16));
+            } else {
+                br.k[rho][c] = Chunk{};
+                br.v[rho][c] = Chunk{};
+            }
+        }
+    }
+}
+
+// Fold one loaded block into the group's online-softmax state.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void process_block(const BlockRegs<BF16, D, G>& br,
+                                              const typename Elem<BF16>::Chunk (&qv)[G][SplitCfg<BF16, D, G>::NC],
+                                              float scale_log2, float (&m)[G], float (&l)[G],
+                                              float (&acc)[G][SplitCfg<BF16, D, G>::DPL]) {
+    typedef SplitCfg<BF16, D, G> C;
+    float s[C::ROWS][G];
+#pragma unroll
+    for (int rho = 0; rho < C::ROWS; rho++) {
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float x = 0.f;
+#pragma unroll
+            for (int c = 0; c < C::NC; c++) x = chunk_dot(qv[h][c], br.k[rho][c], x);
+            x = group8_sum(x);
+            s[rho][h] = br.valid[rho] ? x * scale_log2 : -INFINITY;
+        }
+    }
+    float p[C::ROWS][G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float mx = s[0][h];
+#pragma unroll
+        for (int rho = 1; rho < C::ROWS; rho++) mx = fmaxf(mx, s[rho][h]);
+        if (mx > m[h]) {  // uniform within a group; rare once the max has settled
+            const float alpha = fast_exp2(m[h] - mx);
+            l[h] *= alpha;
+#pragma unroll
+            for (int i = 0; i < C::DPL; i++) acc[h][i] *= alpha;
+            m[h] = mx;
+        }
+#pragma unroll
+        for (int rho = 0; rho < C::ROWS; rho++) {
+            p[rho][h] = fast_exp2(s[rho][h] - m[h]);
+            l[h] += p[rho][h];
+        }
+    }
+#pragma unroll
+    for (int rho = 0; rho < C::ROWS; rho++) {
+#pragma unroll
+        for (int c = 0; c < C::NC; c++) {
+#pragma unroll
+            for (int e = 0; e < C::EPC; e++) {
+                const float ve = chunk_elem(br.v[rho][c], e);
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    acc[h][c * C::EPC + e] = fmaf(p[rho][h], ve, acc[h][c * C::EPC + e]);
+            }
+        }
+    }
+}
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs a) {
+    typedef SplitCfg<BF16, D, G> C;
+    typedef typename Elem<BF16>::Chunk Chunk;
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[2 * kWaves][G];
+    __shared__ float s_acc[2 * kWaves][G * D];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 7;
+    const int g = lane >> 3;
+    const int b = blockIdx.y;
+
+    const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
+    const WorkItem wk = a.work[a.work_begin + blockIdx.x];
+    if (fp != a.fingerprint) return;  // the merge stage reports this as NaN
+    const HeadDesc hd = a.heads[wk.head_index];
+    const int64_t L = a.ctx_len[b];
+    if (L <= 0) return;
+    const int64_t lo = L - hd.window > 0 ? L - hd.window : 0;  // window [lo, L)
+    const int64_t t0 = lo + (int64_t)wk.split * a.split_tokens;
+    if (t0 >= L) return;  // this split lies beyond a window shorter than w
+    const int64_t t1 = t0 + a.split_tokens < L ? t0 + a.split_tokens : L;
+    float* rec = a.ws + ((int64_t)b * a.n_work_range + blockIdx.x) * a.rec_floats;
+
+    const int64_t slot = a.seq_slots ? (int64_t)a.seq_slots[b] : (int64_t)b;
+    if (slot < 0 || slot >= a.table_rows) {  // invalid slot: an empty record -> NaN output
+        for (int e = threadIdx.x; e < G * D; e += kThreads) rec[e] = 0.f;
+        if (threadIdx.x < G) {
+            rec[G * D + threadIdx.x] = -INFINITY;
+            rec[G * D + G + threadIdx.x] = 0.f;
+        }
+        return;
+    }
+    const int32_t* tbl = a.block_ids + slot * a.blocks_per_seq + hd.table_off;
+    const uint32_t nb = (uint32_t)hd.nblocks;
+
+    // query chunks of the G heads of this group
+    Chunk qv[G][C::NC];
+    {
+        const int rel_layer = hd.layer - a.layer_begin;
+        const int64_t qoff =
+            (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
+        const uint8_t* qb = a.q + qoff * C::EB;
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int c = 0; c < C::NC; c++)
+                qv[h][c] = *reinterpret_cast<const Chunk*>(qb + (h * D) * C::EB + (c * 8 + r) * 16);
+    }
+
+    float m[G], l[G], acc[G][C::DPL];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        m[h] = kEmptyMax;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < C::DPL; i++) acc[h][i] = 0.f;
+    }
+
+    const int64_t lb0 = t0 / kBS, lb1 = (t1 - 1) / kBS;  // logical blocks, inclusive
+    int64_t lb = lb0 + wave;
+    uint32_t j = (uint32_t)(lb % nb);  // ring block of lb
+    const uint64_t nblk = a.n_pool_blocks;
+    for (; lb <= lb1; lb += 2 * kWaves) {
+        // ring block of the second block of this iteration
+        uint32_t j2 = j + kWaves;
+        while (j2 >= nb) j2 -= nb;
+        const bool has2 = lb + kWaves <= lb1;
+        const int32_t id1 = tbl[j];
+        const int32_t id2 = has2 ? tbl[j2] : 0;
+        const bool ok1 = id1 >= 0 && (uint64_t)id1 < nblk;
+        const bool ok2 = has2 && id2 >= 0 && (uint64_t)id2 < nblk;
+        BlockRegs<BF16, D, G> b1, b2;
+        load_block<BF16, D, G>(b1, a.pool + (uint64_t)(ok1 ? id1 : 0) * a.block_bytes, ok1, lb,
+                               t0, t1, g, r);
+        load_block<BF16, D, G>(b2, a.pool + (uint64_t)(ok2 ? id2 : 0) * a.block_bytes, ok2,
+                               lb + kWaves, t0, t1, g, r);
+        process_block<BF16, D, G>(b1, qv, a.qk_scale_log2, m, l, acc);
+        if (has2) process_block<BF16, D, G>(b2, qv, a.qk_scale_log2, m, l, acc);
+        j = j2 + kWaves;
+        while (j >= nb) j -= nb;
+    }
+
+    // ---- merge the 32 group states of the workgroup, in a fixed order ----
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float M = m[h];
+        M = fmaxf(M, xor8(M));
+        M = fmaxf(M, xor16(M));
+        M = fmaxf(M, xor32(M));
+        if (lane == 0) s_m[wave][h] = M;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float MW = s_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
+        const float f = fast_exp2(m[h] - MW);
+        float lh = l[h] * f;
+        lh += xor8(lh);
+        lh += xor16(lh);
+#pragma unroll
+        for (int i = 0; i < C::DPL; i++) {
+            float x = acc[h][i] * f;
+            x += xor8(x);
+            x += xor16(x);
+            acc[h][i] = x;
+        }
+        if ((g & 3) == 0) {  // groups 0 and 4 hold the two half-wave sums
+            const int sl = wave * 2 + (g >> 2);
+#pragma unroll
+            for (int c = 0; c < C::NC; c++)
+#pragma unroll
+                for (int e = 0; e < C::EPC; e++)
+                    s_acc[sl][h * D + (c * 8 + r) * C::EPC + e] = acc[h][c * C::EPC + e];
+            if (r == 0) s_l[sl][h] = lh;
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * D; e += kThreads) {
+        float sum = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < 2 * kWaves; sl++) sum += s_acc[sl][e];
+        rec[e] = sum;
+    }
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float MW = s_m[0][h];
+        float lsum = 0.f;
+#pragma unroll
+        for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
+#pragma unroll
+        for (int sl = 0; sl < 2 * kWaves; sl++) lsum += s_l[sl][h];
+        rec[G * D + h] = MW;
+        rec[G * D + G + h] = lsum;
+    }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeMergeArgs a) {
+    const int hrel = blockIdx.x;  // kv head within the layer range
+    const int b = blockIdx.y;
+    const int dim = threadIdx.x;
+    const int rel_layer = hrel / a.n_kv_heads;
+    const int head = hrel % a.n_kv_heads;
+    const int64_t obase =
+        (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)head * G) * D + dim;
+
+    const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
+    const int64_t L = a.ctx_len[b];
+    float o[G];
+    if (fp != a.fingerprint) {
+#pragma unroll
+        for (int h = 0; h < G; h++) o[h] = __builtin_nanf("");
+    } else if (L <= 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++) o[h] = 0.f;
+    } else {
+        const HeadDesc hd = a.heads[a.layer_begin * a.n_kv_heads + hrel];
+        const int64_t n = L < hd.window ? L : hd.window;
+        const int ns = (int)((n + a.split_tokens - 1) / a.split_tokens);
+        const float* rec0 =
+            a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float M = -INFINITY;
+            for (int s = 0; s < ns; s++) M = fmaxf(M, rec0[(int64_t)s * a.rec_floats + G * D + h]);
+            float num = 0.f, den = 0.f;
+            for (int s = 0; s < ns; s++) {
+                const float* rs = rec0 + (int64_t)s * a.rec_floats;
+                const float f = fast_exp2(rs[G * D + h] - M);
+                num = fmaf(f, rs[h * D + dim], num);
+                den = fmaf(f, rs[G * D + G + h], den);
+            }
+            o[h] = num / den;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        if (a.out_bf16)
+            reinterpret_cast<uint16_t*>(a.out)[obase + (int64_t)h * D] = f32_to_bf16_rne(o[h]);
+        else
+            reinterpret_cast<float*>(a.out)[obase + (int64_t)h * D] = o[h];
+    }
+}
+
+template <bool BF16, int D, int G>
+hwkv_status launch_split_t(const DecodeSplitArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_work_range, (unsigned)a.n_seqs);
+    hipLaunchKernelGGL((decode_split_kernel<BF16, D, G>), grid, dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(HWKV_ERR_HIP, std::string("decode split launch: ") + hipGetErrorString(e));
+    return HWKV_OK;
+}
+
+template <int D, int G>
+hwkv_status launch_merge_t(const DecodeMergeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.n_layers * a.n_kv_heads), (unsigned)a.n_seqs);
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), grid, dim3(D), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(HWKV_ERR_HIP, std::string("decode merge launch: ") + hipGetErrorString(e));
+    return HWKV_OK;
+}
+
+// Instances: group sizes 1..4 and 6, 8 for both dtypes and head dims.
+#define HWKV_FOR_GROUPS(X) X(1) X(2) X(3) X(4) X(6) X(8)
+
+}  // namespace
+
+bool decode_supported(hwkv_dtype dt, int head_dim, int group) {
+    if (dt != HWKV_F32 && dt != HWKV_BF16) return false;
+    if (head_dim != 64 && head_dim != 128) return false;
+    switch (group) {
+        case 1: case 2: case 3: case 4: case 6: case 8: return true;
+        default: return false;
+    }
+}
+
+hwkv_status launch_decode_split(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
+                                hipStream_t s) {
+    if (a.n_work_range <= 0) return HWKV_OK;
+    const bool bf16 = lay.dtype == HWKV_BF16;
+#define HWKV_CASE(GG)                                                                      \
+    case GG:                                                                               \
+        if (bf16)                                                                          \
+            return lay.head_dim == 128 ? launch_split_t<true, 128, GG>(a, s)               \
+                                       : launch_split_t<true, 64, GG>(a, s);               \
+        return lay.head_dim == 128 ? launch_split_t<false, 128, GG>(a, s)                  \
+                                   : launch_split_t<false, 64, GG>(a, s);
+    switch (group) {
+        HWKV_FOR_GROUPS(HWKV_CASE)
+        default: break;
+    }
+#undef HWKV_CASE
+    return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for GQA group " + std::to_string(group));
+}
+
+hwkv_status launch_decode_merge(const hwkv_layout& lay, int group, const DecodeMergeArgs& a,
+                                hipStream_t s) {
+#define HWKV_CASE(GG)                                                                        \
+    case GG:                                                                                 \
+        return lay.head_dim == 128 ? launch_merge_t<128, GG>(a, s) : launch_merge_t<64, GG>(a, s);
+    switch (group) {
+        HWKV_FOR_GROUPS(HWKV_CASE)
+        default: break;
+    }
+#undef HWKV_CASE
+    return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for GQA group " + std::to_string(group));
+}
+
+}  // namespace hwkv

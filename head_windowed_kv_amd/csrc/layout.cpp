@@ -1,0 +1,270 @@
+// Host half of libhwkv: layout construction, the exact memory estimate, the
+// default block tables and the device meta blob.  Pure integer arithmetic on
+// the host; no HIP runtime call is made here.
+//
+// Follows the HeadWiseKV write-up (KnoAI), sections 摘要 (static per-head
+// windows make the cache demand exact before serving) and 核心技术 2
+// "Grouped-Cache Runtime" (each head's block table holds
+// ceil(window_size / block_size) blocks; the footprint is computed before
+// the server starts).
+#include <string.h>
+
+#include <limits>
+#include <new>
+#include <string>
+
+#include "hwkv_internal.h"
+
+namespace hwkv {
+
+namespace {
+thread_local std::string g_last_error;
+
+uint64_t fnv1a(uint64_t h, const void* data, size_t n) {
+    const uint8_t* p = static_cast<const uint8_t*>(data);
+    for (size_t i = 0; i < n; i++) {
+        h ^= p[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+bool mul_overflows(uint64_t a, uint64_t b) {
+    return a != 0 && b > std::numeric_limits<uint64_t>::max() / a;
+}
+}  // namespace
+
+hwkv_status fail(hwkv_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace hwkv
+
+using namespace hwkv;
+
+extern "C" {
+
+uint32_t hwkv_abi_version(void) { return HWKV_ABI_VERSION; }
+
+const char* hwkv_last_error(void) { return g_last_error.c_str(); }
+
+hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32_t* windows,
+                               int32_t block_size, int32_t head_dim, hwkv_dtype dtype,
+                               int32_t split_tokens, hwkv_layout** out) {
+    clear_error();
+    if (!out || !windows) return fail(HWKV_ERR_INVALID_ARG, "null windows or out pointer");
+    *out = nullptr;
+    if (n_layers < 1 || n_kv_heads < 1)
+        return fail(HWKV_ERR_INVALID_ARG, "n_layers and n_kv_heads must be >= 1");
+    if ((int64_t)n_layers * n_kv_heads > (1 << 24))
+        return fail(HWKV_ERR_INVALID_ARG, "more than 2^24 heads");
+    if (block_size < 1 || head_dim < 1)
+        return fail(HWKV_ERR_INVALID_ARG, "block_size and head_dim must be >= 1");
+    if (dtype != HWKV_F32 && dtype != HWKV_BF16)
+        return fail(HWKV_ERR_INVALID_ARG, "dtype must be HWKV_F32 or HWKV_BF16");
+    if (block_size != 16)
+        return fail(HWKV_ERR_UNSUPPORTED, "block_size " + std::to_string(block_size) +
+                                              " has no kernel (supported: 16)");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(HWKV_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) +
+                                              " has no kernel (supported: 64, 128)");
+    if (split_tokens == 0) split_tokens = kDefaultSplitTokens;
+    if (split_tokens < block_size || split_tokens % block_size != 0 || split_tokens > (1 << 20))
+        return fail(HWKV_ERR_INVALID_ARG,
+                    "split_tokens must be a multiple of block_size in [block_size, 2^20]");
+
+    const int64_t n_heads = (int64_t)n_layers * n_kv_heads;
+    for (int64_t i = 0; i < n_heads; i++) {
+        if (windows[i] < 1)
+            return fail(HWKV_ERR_INVALID_ARG,
+                        "window < 1 at layer " + std::to_string(i / n_kv_heads) + ", head " +
+                            std::to_string(i % n_kv_heads));
+    }
+
+    hwkv_layout* L = new (std::nothrow) hwkv_layout();
+    if (!L) return fail(HWKV_ERR_INVALID_ARG, "out of host memory");
+    L->n_layers = n_layers;
+    L->n_kv_heads = n_kv_heads;
+    L->block_size = block_size;
+    L->head_dim = head_dim;
+    L->dtype = dtype;
+    L->split_tokens = split_tokens;
+    L->windows.assign(windows, windows + n_heads);
+    L->nblocks.resize(n_heads);
+    L->head_off.resize(n_heads + 1);
+    L->layer_work_off.resize(n_layers + 1);
+    L->heads.resize(n_heads);
+    L->block_bytes = 2ull * block_size * head_dim * elem_bytes(dtype);
+
+    int64_t acc = 0, work = 0;
+    int32_t maxw = 0;
+    for (int64_t i = 0; i < n_heads; i++) {
+        const int64_t w = windows[i];
+        const int64_t nb = (w + block_size - 1) / block_size;  // ceil(w / bs)
+        const int64_t ns = (w + split_tokens - 1) / split_tokens;
+        if (i % n_kv_heads == 0) L->layer_work_off[i / n_kv_heads] = (int32_t)work;
+        L->nblocks[i] = (int32_t)nb;
+        L->head_off[i] = acc;
+        HeadDesc& hd = L->heads[i];
+        hd.table_off = acc;
+        hd.window = (int32_t)w;
+        hd.nblocks = (int32_t)nb;
+        hd.work_off = (int32_t)work;
+        hd.max_splits = (int32_t)ns;
+        hd.layer = (int32_t)(i / n_kv_heads);
+        hd.head = (int32_t)(i % n_kv_heads);
+        acc += nb;
+        work += ns;
+        if (w > maxw) maxw = (int32_t)w;
+        if (work > std::numeric_limits<int32_t>::max() || acc > std::numeric_limits<int32_t>::max()) {
+            delete L;
+            return fail(HWKV_ERR_OVERFLOW, "decode work list or blocks per sequence exceed int32");
+        }
+    }
+    L->head_off[n_heads] = acc;
+    L->layer_work_off[n_layers] = (int32_t)work;
+    L->blocks_per_seq = acc;
+    L->n_work = work;
+    L->max_window = maxw;
+    L->work.resize(work);
+    for (int64_t i = 0; i < n_heads; i++)
+        for (int32_t j = 0; j < L->heads[i].max_splits; j++)
+            L->work[L->heads[i].work_off + j] = WorkItem{(int32_t)i, j};
+
+    uint64_t h = 1469598103934665603ull;
+    const uint32_t abi = HWKV_ABI_VERSION;
+    const int32_t params[6] = {n_layers, n_kv_heads, block_size, head_dim, (int32_t)dtype,
+                               split_tokens};
+    h = fnv1a(h, &abi, sizeof abi);
+    h = fnv1a(h, params, sizeof params);
+    h = fnv1a(h, windows, (size_t)n_heads * sizeof(int32_t));
+    L->fingerprint = h;
+
+    uint64_t off = align_up(sizeof(MetaHeader), kMetaAlign);
+    L->heads_off = off;
+    off = align_up(off + (uint64_t)n_heads * sizeof(HeadDesc), kMetaAlign);
+    L->layer_work_off_bytes = off;
+    off = align_up(off + (uint64_t)(n_layers + 1) * sizeof(int32_t), kMetaAlign);
+    L->work_off = off;
+    off = align_up(off + (uint64_t)work * sizeof(WorkItem), kMetaAlign);
+    L->meta_bytes = off;
+
+    *out = L;
+    return HWKV_OK;
+}
+
+void hwkv_layout_destroy(hwkv_layout* layout) { delete layout; }
+
+hwkv_status hwkv_layout_query(const hwkv_layout* L, hwkv_layout_desc* desc, int32_t* windows_out,
+                              int32_t* nblocks_out, int64_t* head_offsets_out) {
+    clear_error();
+    if (!L) return fail(HWKV_ERR_INVALID_ARG, "null layout");
+    const size_t n_heads = L->windows.size();
+    if (desc) {
+        memset(desc, 0, sizeof *desc);
+        desc->abi_version = HWKV_ABI_VERSION;
+        desc->n_layers = L->n_layers;
+        desc->n_kv_heads = L->n_kv_heads;
+        desc->block_size = L->block_size;
+        desc->head_dim = L->head_dim;
+        desc->dtype = (int32_t)L->dtype;
+        desc->split_tokens = L->split_tokens;
+        desc->max_window = L->max_window;
+        desc->blocks_per_seq = L->blocks_per_seq;
+        desc->n_work = L->n_work;
+        desc->block_bytes = L->block_bytes;
+        desc->meta_bytes = L->meta_bytes;
+        desc->fingerprint = L->fingerprint;
+    }
+    if (windows_out) memcpy(windows_out, L->windows.data(), n_heads * sizeof(int32_t));
+    if (nblocks_out) memcpy(nblocks_out, L->nblocks.data(), n_heads * sizeof(int32_t));
+    if (head_offsets_out)
+        memcpy(head_offsets_out, L->head_off.data(), (n_heads + 1) * sizeof(int64_t));
+    return HWKV_OK;
+}
+
+hwkv_status hwkv_mem_estimate(const hwkv_layout* L, int64_t n_seqs, uint64_t* bytes) {
+    clear_error();
+    if (!L || !bytes) return fail(HWKV_ERR_INVALID_ARG, "null layout or bytes pointer");
+    if (n_seqs < 0) return fail(HWKV_ERR_INVALID_ARG, "n_seqs must be >= 0");
+    // sum over heads of ceil(w/bs) blocks, each block_bytes = 2*bs*d*sizeof
+    const uint64_t per_seq_blocks = (uint64_t)L->blocks_per_seq;
+    if (mul_overflows(per_seq_blocks, L->block_bytes))
+        return fail(HWKV_ERR_OVERFLOW, "per-sequence bytes overflow 64 bits");
+    const uint64_t per_seq = per_seq_blocks * L->block_bytes;
+    if (mul_overflows(per_seq, (uint64_t)n_seqs))
+        return fail(HWKV_ERR_OVERFLOW, "pool bytes overflow 64 bits");
+    *bytes = per_seq * (uint64_t)n_seqs;
+    return HWKV_OK;
+}
+
+hwkv_status hwkv_table_fill(const hwkv_layout* L, int64_t n_seqs, int32_t* block_ids) {
+    clear_error();
+    if (!L || (!block_ids && n_seqs > 0)) return fail(HWKV_ERR_INVALID_ARG, "null argument");
+    if (n_seqs < 0) return fail(HWKV_ERR_INVALID_ARG, "n_seqs must be >= 0");
+    const int64_t bps = L->blocks_per_seq;
+    if (n_seqs > 0 && bps > std::numeric_limits<int32_t>::max() / n_seqs)
+        return fail(HWKV_ERR_OVERFLOW, "block ids exceed int32 for " + std::to_string(n_seqs) +
+                                           " sequences");
+    for (int64_t s = 0; s < n_seqs; s++)
+        for (int64_t j = 0; j < bps; j++) block_ids[s * bps + j] = (int32_t)(s * bps + j);
+    return HWKV_OK;
+}
+
+hwkv_status hwkv_meta_fill(const hwkv_layout* L, void* meta_host, uint64_t meta_bytes) {
+    clear_error();
+    if (!L || !meta_host) return fail(HWKV_ERR_INVALID_ARG, "null argument");
+    if (meta_bytes < L->meta_bytes)
+        return fail(HWKV_ERR_CAPACITY, "meta buffer of " + std::to_string(meta_bytes) +
+                                           " bytes is smaller than " +
+                                           std::to_string(L->meta_bytes));
+    uint8_t* base = static_cast<uint8_t*>(meta_host);
+    memset(base, 0, L->meta_bytes);
+    MetaHeader hdr;
+    memset(&hdr, 0, sizeof hdr);
+    hdr.magic = kMetaMagic;
+    hdr.abi = HWKV_ABI_VERSION;
+    hdr.fingerprint = L->fingerprint;
+    hdr.n_layers = L->n_layers;
+    hdr.n_kv_heads = L->n_kv_heads;
+    hdr.block_size = L->block_size;
+    hdr.head_dim = L->head_dim;
+    hdr.dtype = (int32_t)L->dtype;
+    hdr.split_tokens = L->split_tokens;
+    hdr.blocks_per_seq = L->blocks_per_seq;
+    hdr.n_work = L->n_work;
+    hdr.heads_off = L->heads_off;
+    hdr.layer_work_off = L->layer_work_off_bytes;
+    hdr.work_off = L->work_off;
+    memcpy(base, &hdr, sizeof hdr);
+    memcpy(base + L->heads_off, L->heads.data(), L->heads.size() * sizeof(HeadDesc));
+    memcpy(base + L->layer_work_off_bytes, L->layer_work_off.data(),
+           L->layer_work_off.size() * sizeof(int32_t));
+    memcpy(base + L->work_off, L->work.data(), L->work.size() * sizeof(WorkItem));
+    return HWKV_OK;
+}
+
+hwkv_status hwkv_workspace_bytes(const hwkv_layout* L, int32_t layer_begin, int32_t n_layers,
+                                 int32_t n_seqs, int32_t n_q_heads, uint64_t* bytes) {
+    clear_error();
+    if (!L || !bytes) return fail(HWKV_ERR_INVALID_ARG, "null argument");
+    if (layer_begin < 0 || n_layers < 0 || layer_begin + n_layers > L->n_layers)
+        return fail(HWKV_ERR_INVALID_ARG, "layer range outside the layout");
+    if (n_seqs < 0 || n_q_heads < 1 || n_q_heads % L->n_kv_heads != 0)
+        return fail(HWKV_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+    const int group = n_q_heads / L->n_kv_heads;
+    const uint64_t items =
+        (uint64_t)(L->layer_work_off[layer_begin + n_layers] - L->layer_work_off[layer_begin]);
+    const uint64_t rec = (uint64_t)record_floats(group, L->head_dim) * sizeof(float);
+    if (mul_overflows(items, rec) || mul_overflows(items * rec, (uint64_t)n_seqs))
+        return fail(HWKV_ERR_OVERFLOW, "workspace bytes overflow 64 bits");
+    *bytes = items * rec * (uint64_t)n_seqs;
+    return HWKV_OK;
+}
+
+}  // extern "C"

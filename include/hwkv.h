@@ -1,0 +1,243 @@
+/*
+ * hwkv.h -- C ABI of the per-head windowed KV cache runtime for MI355X (gfx950).
+ *
+ * What it implements.  The HeadWiseKV write-up (KnoAI) gives every physical KV
+ * head of a global-attention layer a static history window w_h and
+ * materialises that policy as real per-head cache residency instead of
+ * masking a full cache (sections 摘要 and 核心技术 2 "Grouped-Cache Runtime").
+ * Each head owns a block table of ceil(w_h / block_size) blocks, so the memory
+ * demand is exact before serving.  This library provides:
+ *   - the layout built from per-layer, per-head window vectors and the exact
+ *     memory estimate (host only);
+ *   - the append of new K/V rows into each head's ring of blocks (device);
+ *   - decode attention over exactly the last w_h tokens of each head, GQA,
+ *     split over the window and merged (device);
+ *   - a chunked-prefill variant: windowed causal attention of a chunk of new
+ *     queries over the cache history plus the chunk itself (device).
+ *
+ * Conventions.
+ *   - Every function returns hwkv_status; hwkv_last_error() gives a message
+ *     for the last failing call on the calling thread.  No exception crosses
+ *     the ABI.
+ *   - Every argument is validated on the host before anything is enqueued:
+ *     a failing call enqueues nothing.
+ *   - Device calls only enqueue kernels on the given HIP stream: no
+ *     allocation, no copy, no synchronisation.  They can be captured in a HIP
+ *     graph.  Stream order is the only ordering between calls.
+ *   - All device memory is owned by the caller.  The library owns only the
+ *     host-side hwkv_layout.
+ *   - A layout is immutable: changing any window means a new layout (and a
+ *     new pool); the write-up's operations table notes that a policy change
+ *     requires a restart.
+ *   - Alignment (write-up "KV Cache Management in Hybrid Attention LLMs",
+ *     section 4.4, which asks for 128- or 256-byte aligned cache pointers):
+ *     pool, block table, meta and workspace pointers must be 256-byte aligned;
+ *     q, k, v and out 16-byte aligned (128-bit accesses); ctx_len/pos0 8-byte
+ *     and seq_slots 4-byte aligned.  Violations return HWKV_ERR_MISALIGNED.
+ *
+ * Memory layout of the pool.  Physical block i occupies bytes
+ * [i*block_bytes, (i+1)*block_bytes): first block_size K rows of head_dim
+ * elements, then block_size V rows.  block_bytes = 2*block_size*head_dim*
+ * sizeof(element).  Token t of a head with nb blocks lives in the head's ring
+ * block (t / block_size) % nb, row t % block_size.
+ *
+ * Block tables.  One int32 row of blocks_per_seq entries per cache slot
+ * ("sequence row"); head (l, h) owns entries [head_off(l,h),
+ * head_off(l,h) + nblocks(l,h)) of the row, heads in layer-major order.  The
+ * ids are physical block indices into the pool; any permutation is allowed.
+ */
+#ifndef HWKV_H
+#define HWKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HWKV_ABI_VERSION 1u
+
+typedef enum hwkv_status {
+    HWKV_OK = 0,
+    HWKV_ERR_INVALID_ARG = 1,  /* bad size, range, null pointer, window < 1 */
+    HWKV_ERR_UNSUPPORTED = 2,  /* a valid configuration this build has no kernel for */
+    HWKV_ERR_MISALIGNED = 3,   /* a pointer breaks the alignment rules above */
+    HWKV_ERR_CAPACITY = 4,     /* pool or workspace smaller than required */
+    HWKV_ERR_ABI_MISMATCH = 5, /* meta blob from another layout or ABI version */
+    HWKV_ERR_HIP = 6,          /* a HIP launch failed */
+    HWKV_ERR_OVERFLOW = 7      /* a size does not fit 64-bit (or int32 ids) */
+} hwkv_status;
+
+typedef enum hwkv_dtype {
+    HWKV_F32 = 0,
+    HWKV_BF16 = 1
+} hwkv_dtype;
+
+typedef struct hwkv_layout hwkv_layout; /* opaque, host-side, immutable */
+
+typedef struct hwkv_layout_desc {
+    uint32_t abi_version;
+    int32_t n_layers;
+    int32_t n_kv_heads;
+    int32_t block_size;
+    int32_t head_dim;
+    int32_t dtype;          /* hwkv_dtype of K, V and q */
+    int32_t split_tokens;   /* decode split length S in tokens */
+    int32_t max_window;
+    int64_t blocks_per_seq; /* entries per block-table row */
+    int64_t n_work;         /* decode work items (head, split) over all layers */
+    uint64_t block_bytes;
+    uint64_t meta_bytes;    /* size of the blob hwkv_meta_fill writes */
+    uint64_t fingerprint;   /* hash of every layout parameter and window */
+} hwkv_layout_desc;
+
+/* Device-side view of one cache.  A host struct of device pointers, passed by
+ * pointer to the device calls. */
+typedef struct hwkv_cache {
+    void *pool;               /* device, pool_bytes bytes, 256-B aligned */
+    uint64_t pool_bytes;      /* must be >= hwkv_mem_estimate(table_rows) */
+    const int32_t *block_ids; /* device [table_rows][blocks_per_seq], 256-B aligned */
+    int64_t table_rows;       /* number of sequence rows (cache slots) */
+    const void *meta;         /* device copy of hwkv_meta_fill, 256-B aligned */
+} hwkv_cache;
+
+/* ABI version compiled into the library (== HWKV_ABI_VERSION of its header).
+ * Page 1 (section 4.2) asks that a kernel reading a cache match the layout of
+ * the kernel that wrote it; callers compare this and the layout fingerprint. */
+uint32_t hwkv_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none).  Capacity
+ * errors name the first head that does not fit, in the form of the write-up's
+ * operations table: "KV cache block allocation failed at layer X, head Y". */
+const char *hwkv_last_error(void);
+
+/* Build a layout from windows[n_layers*n_kv_heads] (layer-major, tokens per
+ * head, each >= 1) -- the per-layer kv_head_windows vectors of the write-up's
+ * policy YAML (核心技术 2).  Each head gets nblocks = ceil(w / block_size)
+ * blocks.  Supported: block_size 16; head_dim 64 or 128; dtype F32 or BF16.
+ * split_tokens is the decode split length S (a multiple of block_size; 0 picks
+ * 512).  On success *out owns the layout; free it with hwkv_layout_destroy.
+ * Errors: INVALID_ARG (null, n < 1, window < 1), UNSUPPORTED, OVERFLOW. */
+hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads,
+                               const int32_t *windows, int32_t block_size,
+                               int32_t head_dim, hwkv_dtype dtype,
+                               int32_t split_tokens, hwkv_layout **out);
+
+void hwkv_layout_destroy(hwkv_layout *layout);
+
+/* Describe a layout.  Optional outputs (may be null): windows_out and
+ * nblocks_out [n_layers*n_kv_heads], head_offsets_out [n_layers*n_kv_heads+1]
+ * (offset of each head's entries inside a block-table row). */
+hwkv_status hwkv_layout_query(const hwkv_layout *layout, hwkv_layout_desc *desc,
+                              int32_t *windows_out, int32_t *nblocks_out,
+                              int64_t *head_offsets_out);
+
+/* Exact pool bytes for n_seqs sequence rows (write-up 摘要 and 核心技术 2:
+ * static per-head windows make the footprint computable before serving):
+ *   n_seqs * sum_{l,h} ceil(w/bs) * bs * head_dim * 2 * sizeof(element).
+ * Covers K and V blocks only (not tables, meta or workspace). */
+hwkv_status hwkv_mem_estimate(const hwkv_layout *layout, int64_t n_seqs,
+                              uint64_t *bytes);
+
+/* Default block tables into host memory block_ids[n_seqs*blocks_per_seq]:
+ * row s gets the consecutive ids [s*blocks_per_seq, (s+1)*blocks_per_seq).
+ * OVERFLOW if an id would not fit int32. */
+hwkv_status hwkv_table_fill(const hwkv_layout *layout, int64_t n_seqs,
+                            int32_t *block_ids);
+
+/* Write the layout's device descriptor blob (per-head windows, block counts,
+ * table offsets and the decode work list) into host memory meta_host of
+ * meta_bytes >= desc.meta_bytes.  The caller copies it to device memory once
+ * and passes that copy as hwkv_cache.meta.  The blob carries the ABI version
+ * and the layout fingerprint; kernels given a blob of another layout write
+ * nothing (append) or NaN (attention). */
+hwkv_status hwkv_meta_fill(const hwkv_layout *layout, void *meta_host,
+                           uint64_t meta_bytes);
+
+/* Device workspace needed by hwkv_decode_split/_merge/_attn for layers
+ * [layer_begin, layer_begin+n_layers), n_seqs sequences and n_q_heads query
+ * heads: one fp32 record (acc[G][d], m[G], l[G]) per (sequence, work item). */
+hwkv_status hwkv_workspace_bytes(const hwkv_layout *layout, int32_t layer_begin,
+                                 int32_t n_layers, int32_t n_seqs,
+                                 int32_t n_q_heads, uint64_t *bytes);
+
+/* Append n_new tokens per sequence: positions [pos0[b], pos0[b]+n_new) of
+ * layers [layer_begin, layer_begin+n_layers).  k, v: device
+ * [n_layers][n_seqs][n_new][n_kv_heads][head_dim] in the layout's dtype.
+ * seq_slots: device int32[n_seqs], the table row of each batch entry, or null
+ * for row b.  pos0: device int64[n_seqs].  Each head keeps only its most
+ * recent tokens (page 2, "SWA Window": the window shifts as the sequence
+ * advances): a head with ring capacity C stores token t in ring block
+ * (t/bs)%nblocks, row t%bs, and of this call's tokens only those with
+ * t >= pos0+n_new-C are written (older ones would be overwritten in the same
+ * call).  Bit copies, no arithmetic.  Device values out of range (slot
+ * outside the table, negative position, block id outside the pool) make the
+ * affected rows be skipped, never an out-of-bounds access. */
+hwkv_status hwkv_append(const hwkv_layout *layout, const hwkv_cache *cache,
+                        int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                        const int32_t *seq_slots, const int64_t *pos0,
+                        int32_t n_new, const void *k, const void *v,
+                        hipStream_t stream);
+
+/* Decode attention, first stage: for each (layer, sequence b, kv head h) the
+ * window [max(0, L-w), L) with L = ctx_len[b] (the newest token already
+ * appended) is cut into splits of split_tokens tokens; each split writes
+ * running max m, sum l and acc = sum_t 2^(s_t-m) v_t for the G = n_q_heads /
+ * n_kv_heads query heads of the group (query head i reads kv head i / G),
+ * s_t = log2(e) * scale * q_i . k_t.  q: device [n_layers][n_seqs][n_q_heads]
+ * [head_dim] in the layout's dtype.  workspace: hwkv_workspace_bytes. */
+hwkv_status hwkv_decode_split(const hwkv_layout *layout, const hwkv_cache *cache,
+                              int32_t layer_begin, int32_t n_layers,
+                              int32_t n_seqs, const int32_t *seq_slots,
+                              const int64_t *ctx_len, int32_t n_q_heads,
+                              const void *q, float scale, void *workspace,
+                              uint64_t workspace_bytes, hipStream_t stream);
+
+/* Decode attention, second stage: per (layer, sequence, query head) combine
+ * the splits: M = max m_s, o = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
+ * out: device [n_layers][n_seqs][n_q_heads][head_dim] as out_dtype.  A
+ * sequence with ctx_len <= 0 gets zeros.  Same layer range, n_seqs, ctx_len
+ * and workspace as the split stage. */
+hwkv_status hwkv_decode_merge(const hwkv_layout *layout, const hwkv_cache *cache,
+                              int32_t layer_begin, int32_t n_layers,
+                              int32_t n_seqs, const int64_t *ctx_len,
+                              int32_t n_q_heads, const void *workspace,
+                              uint64_t workspace_bytes, void *out,
+                              hwkv_dtype out_dtype, hipStream_t stream);
+
+/* Decode attention over exactly the last w_h tokens of every head (write-up
+ * 摘要: per-head residency, not a mask): hwkv_decode_split followed by
+ * hwkv_decode_merge on the same stream.  Call hwkv_append for the new token
+ * first. */
+hwkv_status hwkv_decode_attn(const hwkv_layout *layout, const hwkv_cache *cache,
+                             int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                             const int32_t *seq_slots, const int64_t *ctx_len,
+                             int32_t n_q_heads, const void *q, float scale,
+                             void *workspace, uint64_t workspace_bytes, void *out,
+                             hwkv_dtype out_dtype, hipStream_t stream);
+
+/* Chunked prefill of one layer: sequence b has history [0, P) in the cache,
+ * P = pos0[b], and n_chunk new tokens at [P, P+n_chunk).  Query row r
+ * (position p = P + r) of query head i attends to kv head i / G over
+ * [max(0, p-w+1), p]: keys before P are read from the cache (only the last
+ * w-1 of them can be needed, and the ring holds at least w), keys from P on
+ * from k, v.  q: device [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: device
+ * [n_seqs][n_chunk][n_kv_heads][head_dim]; out: [n_seqs][n_chunk][n_q_heads]
+ * [head_dim] as out_dtype.  The cache is read, not written: call hwkv_append
+ * with the same k, v (n_layers = 1) afterwards, since appending first could
+ * overwrite history that earlier rows of the chunk still need.  BF16 layouts
+ * with head_dim 128 use MFMA tiles. */
+hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache,
+                              int32_t layer, int32_t n_seqs,
+                              const int32_t *seq_slots, const int64_t *pos0,
+                              int32_t n_chunk, int32_t n_q_heads, const void *q,
+                              const void *k, const void *v, void *out,
+                              hwkv_dtype out_dtype, float scale,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HWKV_H */

@@ -1,0 +1,199 @@
+"""Host half of the C ABI, on the CPU: the library loads, exports every symbol
+its header declares, and its layout arithmetic is bit-exact against the
+oracle.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+hw = pytest.importorskip("head_windowed_kv_amd", reason="libhwkv.so not built")
+
+CONFIG_WINDOWS = {
+    "tiny": np.array([[32, 128]], np.int32),
+    "single_layer": np.array([synth.YAML_LAYER0], np.int32),
+    "stack48": synth.stack_windows(48, 8, 0),
+    "yaml_two_layers": np.array([synth.YAML_LAYER0, synth.YAML_LAYER1], np.int32),
+}
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "hwkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hwkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hw.LIB_PATH)
+    declared = _declared_symbols()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(hw.EXPORTED) == declared
+
+
+def test_abi_version():
+    assert hw.hwkv_abi_version() == hw.ABI_VERSION == 1
+
+
+@pytest.mark.parametrize("name", sorted(CONFIG_WINDOWS))
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_layout_and_estimate_bit_exact_vs_oracle(name, dtype, d):
+    w = CONFIG_WINDOWS[name]
+    lay = hw.hwkv_layout_create(w, 16, d, dtype)
+    desc, w_out, nb, off = hw.hwkv_layout_query(lay)
+    onb, ooff, obps = oracle.layout(w, 16)
+    assert np.array_equal(w_out, w)
+    assert np.array_equal(nb.reshape(-1), onb)
+    assert np.array_equal(off, ooff)
+    assert desc.blocks_per_seq == obps
+    eb = 2 if dtype == "bf16" else 4
+    assert desc.block_bytes == 2 * 16 * d * eb
+    for n in (1, 3, 32):
+        assert hw.hwkv_mem_estimate(lay, n) == oracle.mem_estimate(w, 16, d, eb, n)
+    assert np.array_equal(hw.hwkv_table_fill(lay, 3), oracle.default_table(3, obps))
+
+
+def test_stack48_seed0_numbers():
+    """The 48-layer synthetic stack: level counts and exact pool bytes."""
+    w = synth.stack_windows(48, 8, 0)
+    counts = {lv: int((w == lv).sum()) for lv in synth.WINDOW_LEVELS}
+    assert counts == {1024: 79, 4096: 98, 16384: 114, 65536: 93}
+    assert int(w.sum()) == 8444928
+    lay = hw.hwkv_layout_create(w, 16, 128, "bf16")
+    assert hw.hwkv_mem_estimate(lay, 1) == 4323803136
+    assert hw.hwkv_mem_estimate(lay, 32) == 138361700352
+
+
+def test_random_windows_bit_exact():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        nl, nh = rng.integers(1, 6), rng.integers(1, 9)
+        w = rng.integers(1, 70000, size=(nl, nh)).astype(np.int32)
+        w[rng.random(w.shape) < 0.2] = 1
+        lay = hw.hwkv_layout_create(w, 16, 128, "bf16", split_tokens=int(rng.choice([16, 256, 512])))
+        desc, _, nb, off = hw.hwkv_layout_query(lay)
+        onb, ooff, obps = oracle.layout(w, 16)
+        assert np.array_equal(nb.reshape(-1), onb) and np.array_equal(off, ooff)
+        assert hw.hwkv_mem_estimate(lay, 7) == oracle.mem_estimate(w, 16, 128, 2, 7)
+        splits = -(-w.astype(np.int64) // desc.split_tokens)
+        assert desc.n_work == int(splits.sum())
+        assert desc.max_window == int(w.max())
+
+
+def test_workspace_bytes():
+    w = np.array([[1024, 4096], [100, 1]], np.int32)
+    lay = hw.hwkv_layout_create(w, 16, 128, "bf16", split_tokens=512)
+    # splits: 2 + 8 + 1 + 1 = 12 items; record = 3*(128+2) = 390 -> 392 floats
+    assert hw.hwkv_workspace_bytes(lay, 0, 2, 5, 6) == 12 * 392 * 4 * 5
+    assert hw.hwkv_workspace_bytes(lay, 1, 1, 1, 6) == 2 * 392 * 4
+    assert hw.hwkv_workspace_bytes(lay, 0, 1, 1, 2) == 10 * 132 * 4
+
+
+def test_meta_blob_header():
+    lay = hw.hwkv_layout_create(CONFIG_WINDOWS["tiny"], 16, 64, "f32")
+    meta = hw.hwkv_meta_fill(lay)
+    desc = lay.desc()
+    assert meta.size == desc.meta_bytes and meta.size % 256 == 0
+    assert int(meta[:4].view(np.uint32)[0]) == 0x564B5748
+    assert int(meta[4:8].view(np.uint32)[0]) == 1
+    assert int(meta[8:16].view(np.uint64)[0]) == desc.fingerprint
+
+
+def test_fingerprint_tracks_every_parameter():
+    base = hw.hwkv_layout_create([[32, 128]], 16, 64, "f32").desc().fingerprint
+    others = [hw.hwkv_layout_create([[32, 129]], 16, 64, "f32"),
+              hw.hwkv_layout_create([[32, 128]], 16, 128, "f32"),
+              hw.hwkv_layout_create([[32, 128]], 16, 64, "bf16"),
+              hw.hwkv_layout_create([[32, 128]], 16, 64, "f32", split_tokens=32),
+              hw.hwkv_layout_create([[32], [128]], 16, 64, "f32")]
+    fps = {o.desc().fingerprint for o in others}
+    assert base not in fps and len(fps) == len(others)
+
+
+@pytest.mark.parametrize("args,status", [
+    (([[0, 4]], 16, 128, "bf16"), "HWKV_ERR_INVALID_ARG"),
+    (([[-5]], 16, 128, "bf16"), "HWKV_ERR_INVALID_ARG"),
+    (([[16]], 32, 128, "bf16"), "HWKV_ERR_UNSUPPORTED"),
+    (([[16]], 16, 96, "bf16"), "HWKV_ERR_UNSUPPORTED"),
+    (([[16]], 16, 128, "bf16", 24), "HWKV_ERR_INVALID_ARG"),
+])
+def test_layout_create_errors(args, status):
+    with pytest.raises(hw.HwkvError) as e:
+        hw.hwkv_layout_create(*args)
+    assert e.value.status_name == status
+
+
+def test_table_fill_overflow_is_reported():
+    lay = hw.hwkv_layout_create([[65536] * 8], 16, 128, "bf16")
+    with pytest.raises(hw.HwkvError) as e:
+        hw.hwkv_table_fill(lay, 100000)
+    assert e.value.status_name == "HWKV_ERR_OVERFLOW"
+
+
+def _fake_cache(lay, pool_bytes, rows, pool_ptr=1 << 20):
+    # device pointers are never dereferenced: validation fails first
+    return hw.hwkv_cache(pool_ptr, pool_bytes, 2 << 20, rows, 3 << 20)
+
+
+def test_capacity_error_names_layer_and_head():
+    w = np.array([synth.YAML_LAYER0, synth.YAML_LAYER1], np.int32)
+    lay = hw.hwkv_layout_create(w, 16, 128, "bf16")
+    need = hw.hwkv_mem_estimate(lay, 2)
+    bb = lay.desc().block_bytes
+    # room for row 0 and the first 18944 + 100 blocks of row 1: row 1 stops in
+    # layer 1, head 0 (offset 18944, 64 blocks) -> head 1 (offset 19008) fails
+    avail_blocks = lay.desc().blocks_per_seq + 18944 + 100
+    cv = _fake_cache(lay, avail_blocks * bb, 2)
+    pos = ctypes.c_void_p(4 << 20)
+    st = hw._lib.hwkv_append(lay.handle, ctypes.byref(cv), 0, 1, 1, None, pos, 1,
+                             ctypes.c_void_p(5 << 20), ctypes.c_void_p(6 << 20), None)
+    assert hw.STATUS_NAMES[st] == "HWKV_ERR_CAPACITY"
+    msg = hw.hwkv_last_error()
+    assert "KV cache block allocation failed at layer 1, head 1" in msg
+    assert str(need) in msg
+
+
+def test_misaligned_pool_is_rejected_before_launch():
+    lay = hw.hwkv_layout_create([[32, 128]], 16, 64, "f32")
+    cv = _fake_cache(lay, hw.hwkv_mem_estimate(lay, 1), 1, pool_ptr=(1 << 20) + 64)
+    st = hw._lib.hwkv_append(lay.handle, ctypes.byref(cv), 0, 1, 1, None, ctypes.c_void_p(4 << 20),
+                             1, ctypes.c_void_p(5 << 20), ctypes.c_void_p(6 << 20), None)
+    assert hw.STATUS_NAMES[st] == "HWKV_ERR_MISALIGNED"
+
+
+def test_decode_argument_errors_before_launch():
+    lay = hw.hwkv_layout_create([[32, 128]], 16, 64, "f32")
+    cv = _fake_cache(lay, hw.hwkv_mem_estimate(lay, 1), 1)
+    ws = ctypes.c_void_p(8 << 20)
+    q = ctypes.c_void_p(9 << 20)
+    ctx = ctypes.c_void_p(10 << 20)
+    out = ctypes.c_void_p(11 << 20)
+    need = hw.hwkv_workspace_bytes(lay, 0, 1, 1, 4)
+    f = hw._lib.hwkv_decode_attn
+    # n_q_heads not a multiple of n_kv_heads
+    assert f(lay.handle, ctypes.byref(cv), 0, 1, 1, None, ctx, 3, q, 0.1, ws, need, out, 0,
+             None) == 1
+    # workspace too small
+    assert f(lay.handle, ctypes.byref(cv), 0, 1, 1, None, ctx, 4, q, 0.1, ws, need - 4, out, 0,
+             None) == 4
+    # layer range outside the layout
+    assert f(lay.handle, ctypes.byref(cv), 0, 2, 1, None, ctx, 4, q, 0.1, ws, need, out, 0,
+             None) == 1
+    # more sequences than table rows without seq_slots
+    assert f(lay.handle, ctypes.byref(cv), 0, 1, 2, None, ctx, 4, q, 0.1, ws, need, out, 0,
+             None) == 1
+    # unsupported GQA group (5)
+    lay5 = hw.hwkv_layout_create([[32]], 16, 64, "f32")
+    cv5 = _fake_cache(lay5, hw.hwkv_mem_estimate(lay5, 1), 1)
+    assert f(lay5.handle, ctypes.byref(cv5), 0, 1, 1, None, ctx, 5, q, 0.1, ws, 1 << 20, out, 0,
+             None) == 2
+    # non-finite scale
+    assert f(lay.handle, ctypes.byref(cv), 0, 1, 1, None, ctx, 4, q, float("inf"), ws, need, out,
+             0, None) == 1
