@@ -43,6 +43,12 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--counter-pass", action="store_true",
+                   help="short run for a rocprofv3 --pmc pass: a few steps plus one probe "
+                        "copy of known size (the counters' calibration)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
+                        "into profiles/decode_split_stack48_counters.json and exit")
     return p.parse_args()
 
 
@@ -54,21 +60,134 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(split_launch_bytes: float):
+def load_traffic(split_tokens: int):
     """HBM traffic of one split launch from committed rocprofv3 counter runs,
-    valid only while the kernel source is the one the counters were taken on."""
+    valid only while the kernel source and split size are the ones the
+    counters were taken on."""
     path = os.path.join(ROOT, "profiles", "decode_split_stack48_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+    if rec.get("kernel_source_sha") != kernel_source_sha() or \
+            rec.get("split_tokens") != split_tokens:
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
+PROBE_COPY_BYTES = 1 << 30
+
+
+def probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "head_windowed_kv_amd", "libhwkv_probe.so"))
+    lib.hwkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_void_p]
+    lib.hwkv_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                    ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+def read_ceiling(torch, buf):
+    """Practical HBM read bandwidth: a plain streaming read over `buf`."""
+    import ctypes
+    lib = probe_lib()
+    s = torch.cuda.current_stream()
+    out = torch.zeros(4, dtype=torch.uint8, device=buf.device)
+    n = buf.numel() // 16 * 16
+    best = 0.0
+    for grid in (2048, 16384):
+        ts = []
+        for _ in range(6):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            rc = lib.hwkv_probe_read(ctypes.c_void_p(buf.data_ptr()), n,
+                                     ctypes.c_void_p(out.data_ptr()), grid,
+                                     ctypes.c_void_p(s.cuda_stream))
+            e1.record(s)
+            torch.cuda.synchronize()
+            assert rc == 0
+            ts.append(e0.elapsed_time(e1))
+        best = max(best, n / (sorted(ts)[len(ts) // 2] / 1e3) / 1e9)
+    return best
+
+
+def probe_copy_once(torch, dev):
+    import ctypes
+    lib = probe_lib()
+    src = torch.ones(PROBE_COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    s = torch.cuda.current_stream()
+    rc = lib.hwkv_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                             PROBE_COPY_BYTES, 4096, ctypes.c_void_p(s.cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == 0
+
+
+def _pmc_rows(folder, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc output folder
+    (CSV or SQLite)."""
+    import csv
+    import glob
+    import sqlite3
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if rows:
+        return rows
+    for f in glob.glob(os.path.join(folder, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(f)
+        q = ("select k.name, p.value from pmc_events p join kernels k on p.event_id = k.id "
+             "where p.counter_name = ?")
+        try:
+            rows += [(n, float(v)) for n, v in con.execute(q, (counter,))]
+        except sqlite3.Error:
+            cols = [c[1] for c in con.execute("pragma table_info(counters_collection)")]
+            name_col = "kernel_name" if "kernel_name" in cols else "name"
+            q = "select %s, value from counters_collection where counter_name = ?" % name_col
+            rows += [(n, float(v)) for n, v in con.execute(q, (counter,))]
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, split_tokens):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel, each
+    scaled by what the same counter reads for the probe copy of known size."""
+    import head_windowed_kv_amd as H
+    import synth
+    lay = H.hwkv_layout_create(synth.stack_windows(48, 8, 0), 16, 128, "bf16", split_tokens)
+    out = {"kernel_source_sha": kernel_source_sha(), "probe_copy_bytes": PROBE_COPY_BYTES,
+           "split_tokens": lay.desc().split_tokens,
+           "command": "rocprofv3 --pmc <COUNTER> --output-format csv -d <dir> -o run -- "
+                      "python -u bench.py --counter-pass --steps 3 --warmup 1"}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(folder, counter)
+        split = [v for n, v in rows if "decode_split_kernel" in n]
+        copy = [v for n, v in rows if "probe_copy_kernel" in n]
+        if not split or not copy:
+            raise SystemExit("no %s rows for the split or the probe copy in %s" % (counter, folder))
+        split_kib = sorted(split)[len(split) // 2]
+        copy_kib = copy[-1]
+        scale = PROBE_COPY_BYTES / (copy_kib * 1024.0)
+        out[counter] = {"split_kib_per_dispatch": split_kib, "probe_copy_kib": copy_kib,
+                        "scale": round(scale, 4), "split_bytes_scaled": split_kib * 1024 * scale,
+                        "dispatches": len(split)}
+    out["traffic_bytes_per_launch"] = (out["FETCH_SIZE"]["split_bytes_scaled"] +
+                                       out["WRITE_SIZE"]["split_bytes_scaled"])
+    path = os.path.join(ROOT, "profiles", "decode_split_stack48_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.split_tokens)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -136,6 +255,12 @@ def main():
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
+    if args.counter_pass:
+        for j in range(args.steps):
+            run_step(args.warmup + j)
+        probe_copy_once(torch, dev)
+        print(json.dumps({"counter_pass": True, "steps": args.steps}), flush=True)
+        return
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -184,12 +309,15 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(bytes_step),
+            "traffic": load_traffic(desc.split_tokens),
             "avg_launch_ms": round(split_avg_ms, 4),
             "algorithmic_bytes_per_launch": bytes_step,
         },
         "fill_seconds": round(t_fill, 2),
     }
+    ceiling = read_ceiling(torch, cache.pool)
+    result["practical_read_ceiling_gbps"] = round(ceiling, 1)
+    result["roofline"]["frac_of_practical_ceiling"] = round(split_gbps / ceiling, 4)
 
     if not args.no_graph:
         result["per_layer_graph"] = per_layer_graph(H, torch, cache, lay, windows, q, k_new,

@@ -142,9 +142,9 @@ class Layout:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and not getattr(self, "_freed", False):
+            self._freed = True
             self._destroy(h)
-            self._h = ctypes.c_void_p(0)
 
     def desc(self) -> hwkv_layout_desc:
         return hwkv_layout_query(self)[0]

@@ -13,6 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhwkv.so")
+PROBE_LIB = os.path.join(PKG, "libhwkv_probe.so")
 
 SOURCES = ["layout.cpp", "api.cpp", "append.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
@@ -54,14 +55,22 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + ["probe.hip"]))
+    probe_obj = objs.pop()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
+    # HBM reference kernels used by the benchmark, in a library of their own
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, probe_obj, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

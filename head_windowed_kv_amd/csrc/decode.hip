@@ -4,11 +4,12 @@
 // own block table of ceil(w_h / block_size) blocks).
 //
 // Stage 1 (split): one workgroup per (work item = (layer, kv head, split),
-// sequence).  A split is split_tokens consecutive positions of the window
-// [max(0, L-w), L); the workgroup streams the K/V rows of those positions
-// through the head's ring of blocks and keeps, for the G query heads of the
-// GQA group, an online-softmax state (running max m, sum l, weighted sum acc)
-// in registers.  Decode is HBM-bound (about 3 flop per byte read), so there
+// sequence).  A split is a run of split_tokens/16 consecutive logical blocks
+// of the window [max(0, L-w), L) (cut on block boundaries, the last split
+// taking the remainder); the workgroup streams those K/V blocks through the
+// head's ring and keeps, for the G query heads of the GQA group, an
+// online-softmax state (running max m, sum l, weighted sum acc) in
+// registers.  Decode is HBM-bound (about 3 flop per byte read), so there
 // is no MFMA here: the design goal is to keep enough 128-bit loads in flight.
 //
 // Work layout inside a workgroup (256 threads = 4 wave64):
@@ -148,46 +149,42 @@ struct BlockRegs {
     typedef SplitCfg<BF16, D, G> C;
     Chunk k[C::ROWS][C::NC];
     Chunk v[C::ROWS][C::NC];
-    bool valid[C::ROWS];
 };
 
 // Issue the loads of one block for this lane (rows g + 8*rho, chunks r + 8*c).
+// Loads are unconditional: `blk` always points at a block inside the pool
+// (block 0 stands in for an invalid id), and rows outside the split are
+// masked when the block is folded in.
 template <bool BF16, int D, int G>
-__device__ __forceinline__ void load_block(BlockRegs<BF16, D, G>& br, const uint8_t* blk,
-                                           bool blk_ok, int64_t lb, int64_t t0, int64_t t1,
-                                           int g, int r) {
+__device__ __forceinline__ void load_block(BlockRegs<BF16, D, G>& br, const uint8_t* blk, int g,
+                                           int r) {
     typedef SplitCfg<BF16, D, G> C;
     typedef typename Elem<BF16>::Chunk Chunk;
 #pragma unroll
     for (int rho = 0; rho < C::ROWS; rho++) {
-        const int row = g + 8 * rho;
-        const int64_t pos = lb * kBS + row;
-        const bool ok = blk_ok && pos >= t0 && pos < t1;
-        br.valid[rho] = ok;
-        const uint8_t* krow = blk + row * C::ROW;
+        const uint8_t* krow = blk + (g + 8 * rho) * C::ROW;
         const uint8_t* vrow = krow + kBS * C::ROW;
 #pragma unroll
         for (int c = 0; c < C::NC; c++) {
-            if (ok) {
-                br.k[rho][c] = __builtin_nontemporal_load(
-                    reinterpret_cast<const Chunk*>(krow + (c * 8 + r) * 16));
-                br.v[rho][c] = __builtin_nontemporal_load(
-                    reinterpret_cast<const Chunk*>(vrow + (c * 8 + r) * 16));
-            } else {
-                br.k[rho][c] = Chunk{};
-                br.v[rho][c] = Chunk{};
-            }
+            br.k[rho][c] =
+                __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(krow + (c * 8 + r) * 16));
+            br.v[rho][c] =
+                __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vrow + (c * 8 + r) * 16));
         }
     }
 }
 
-// Fold one loaded block into the group's online-softmax state.
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void process_block(const BlockRegs<BF16, D, G>& br,
+// Fold one loaded block into the group's online-softmax state.  FULL: every
+// row of the block lies in the split (the common case, no masking).
+// Otherwise row rho is used only if valid[rho]; its V chunk is zeroed so that
+// stale or uninitialised pool bytes cannot leak in as NaN * 0.
+template <bool BF16, int D, int G, bool FULL>
+__device__ __forceinline__ void process_block(BlockRegs<BF16, D, G>& br, const bool* valid,
                                               const typename Elem<BF16>::Chunk (&qv)[G][SplitCfg<BF16, D, G>::NC],
                                               float scale_log2, float (&m)[G], float (&l)[G],
                                               float (&acc)[G][SplitCfg<BF16, D, G>::DPL]) {
     typedef SplitCfg<BF16, D, G> C;
+    typedef typename Elem<BF16>::Chunk Chunk;
     float s[C::ROWS][G];
 #pragma unroll
     for (int rho = 0; rho < C::ROWS; rho++) {
@@ -197,7 +194,11 @@ __device__ __forceinline__ void process_block(const BlockRegs<BF16, D, G>& br,
 #pragma unroll
             for (int c = 0; c < C::NC; c++) x = chunk_dot(qv[h][c], br.k[rho][c], x);
             x = group8_sum(x);
-            s[rho][h] = br.valid[rho] ? x * scale_log2 : -INFINITY;
+            s[rho][h] = (FULL || valid[rho]) ? x * scale_log2 : -INFINITY;
+        }
+        if (!FULL && !valid[rho]) {
+#pragma unroll
+            for (int c = 0; c < C::NC; c++) br.v[rho][c] = Chunk{};
         }
     }
     float p[C::ROWS][G];
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     __shared__ float s_acc[2 * kWaves][G * D];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 7;
     const int g = lane >> 3;
     const int b = blockIdx.y;
@@ -254,10 +255,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     const HeadDesc hd = a.heads[wk.head_index];
     const int64_t L = a.ctx_len[b];
     if (L <= 0) return;
-    const int64_t lo = L - hd.window > 0 ? L - hd.window : 0;  // window [lo, L)
-    const int64_t t0 = lo + (int64_t)wk.split * a.split_tokens;
-    if (t0 >= L) return;  // this split lies beyond a window shorter than w
-    const int64_t t1 = t0 + a.split_tokens < L ? t0 + a.split_tokens : L;
+    // Window [lo, L).  Splits are cut on block boundaries: split j covers
+    // the logical blocks [bA + j*SB, bA + (j+1)*SB) with bA = lo / 16 and
+    // SB = split_tokens / 16, except that the last split runs to the
+    // window's last block.  So only the window's first and last blocks are
+    // partial, and the number of splits is ceil(min(w, L) / split_tokens),
+    // fixed by (w, L) alone.
+    const int64_t lo = L - hd.window > 0 ? L - hd.window : 0;
+    const int64_t n_win = L - lo;
+    const int64_t ns = (n_win + a.split_tokens - 1) / a.split_tokens;
+    if (wk.split >= ns) return;  // beyond a window shorter than w
+    const int64_t SB = a.split_tokens / kBS;
+    const int64_t bA = lo / kBS, bZ = (L - 1) / kBS;
+    const int64_t lb0 = bA + (int64_t)wk.split * SB;
+    const int64_t lb1 = wk.split == ns - 1 ? bZ : lb0 + SB - 1;
     float* rec = a.ws + ((int64_t)b * a.n_work_range + blockIdx.x) * a.rec_floats;
 
     const int64_t slot = a.seq_slots ? (int64_t)a.seq_slots[b] : (int64_t)b;
@@ -271,6 +282,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     }
     const int32_t* tbl = a.block_ids + slot * a.blocks_per_seq + hd.table_off;
     const uint32_t nb = (uint32_t)hd.nblocks;
+
+    // Blocks of the split: logical blocks [lb0, lb1]; wave w takes lb0 + w,
+    // lb0 + w + 4, ...  Lane i of the wave preloads the physical id of its
+    // i-th block, so the loop reads ids with readlane and never waits on
+    // the block table.
+    const int nblk = (int)(lb1 - lb0 + 1);
+    const int my_n = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+    int32_t my_id = -1;
+    if (lane < my_n) {
+        const uint32_t j = (uint32_t)((lb0 + wave + (int64_t)lane * kWaves) % nb);
+        my_id = tbl[j];
+    }
 
     // query chunks of the G heads of this group
     Chunk qv[G][C::NC];
@@ -295,28 +318,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         for (int i = 0; i < C::DPL; i++) acc[h][i] = 0.f;
     }
 
-    const int64_t lb0 = t0 / kBS, lb1 = (t1 - 1) / kBS;  // logical blocks, inclusive
-    int64_t lb = lb0 + wave;
-    uint32_t j = (uint32_t)(lb % nb);  // ring block of lb
-    const uint64_t nblk = a.n_pool_blocks;
-    for (; lb <= lb1; lb += 2 * kWaves) {
-        // ring block of the second block of this iteration
-        uint32_t j2 = j + kWaves;
-        while (j2 >= nb) j2 -= nb;
-        const bool has2 = lb + kWaves <= lb1;
-        const int32_t id1 = tbl[j];
-        const int32_t id2 = has2 ? tbl[j2] : 0;
-        const bool ok1 = id1 >= 0 && (uint64_t)id1 < nblk;
-        const bool ok2 = has2 && id2 >= 0 && (uint64_t)id2 < nblk;
-        BlockRegs<BF16, D, G> b1, b2;
-        load_block<BF16, D, G>(b1, a.pool + (uint64_t)(ok1 ? id1 : 0) * a.block_bytes, ok1, lb,
-                               t0, t1, g, r);
-        load_block<BF16, D, G>(b2, a.pool + (uint64_t)(ok2 ? id2 : 0) * a.block_bytes, ok2,
-                               lb + kWaves, t0, t1, g, r);
-        process_block<BF16, D, G>(b1, qv, a.qk_scale_log2, m, l, acc);
-        if (has2) process_block<BF16, D, G>(b2, qv, a.qk_scale_log2, m, l, acc);
-        j = j2 + kWaves;
-        while (j >= nb) j -= nb;
+    const uint64_t nblk_pool = a.n_pool_blocks;
+    // physical block i of this wave (block 0 stands in for an invalid id)
+    auto block_ptr = [&](int i, bool& ok) -> const uint8_t* {
+        const int32_t id = __builtin_amdgcn_readlane(my_id, i);
+        ok = id >= 0 && (uint64_t)id < nblk_pool;
+        return a.pool + (uint64_t)(ok ? id : 0) * a.block_bytes;
+    };
+    auto fold = [&](BlockRegs<BF16, D, G>& br, int i, bool ok) {
+        const int64_t lb = lb0 + wave + (int64_t)i * kWaves;
+        const int64_t first = lb * kBS;
+        if (ok && first >= lo && first + kBS <= L) {
+            process_block<BF16, D, G, true>(br, nullptr, qv, a.qk_scale_log2, m, l, acc);
+        } else {
+            bool valid[C::ROWS];
+#pragma unroll
+            for (int rho = 0; rho < C::ROWS; rho++) {
+                const int64_t pos = first + g + 8 * rho;
+                valid[rho] = ok && pos >= lo && pos < L;
+            }
+            process_block<BF16, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
+        }
+    };
+
+    // Two blocks per iteration: both blocks' loads (16 KiB per wave) are
+    // issued before either is folded in.
+    for (int i = 0; i < my_n; i += 2) {
+        BlockRegs<BF16, D, G> bufA, bufB;
+        bool okA, okB = false;
+        load_block<BF16, D, G>(bufA, block_ptr(i, okA), g, r);
+        if (i + 1 < my_n) load_block<BF16, D, G>(bufB, block_ptr(i + 1, okB), g, r);
+        fold(bufA, i, okA);
+        if (i + 1 < my_n) fold(bufB, i + 1, okB);
     }
 
     // ---- merge the 32 group states of the workgroup, in a fixed order ----
@@ -375,51 +408,120 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     }
 }
 
+// Merge geometry: one thread per float4 of a record's acc[G][D] (NE4 of
+// them) times SG split groups; split s is folded by group s % SG, and the SG
+// partial sums are added in a fixed order.  Many splits are read in parallel
+// instead of one after another.
 template <int D, int G>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeMergeArgs a) {
+struct MergeCfg {
+    static constexpr int NE4 = G * D / 4;
+    static constexpr int SG = (1024 / NE4) < 16 ? (1024 / NE4) : 16;
+    static constexpr int THREADS = NE4 * SG;
+    static constexpr int WAVES = (THREADS + 63) / 64;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel(DecodeMergeArgs a) {
+    typedef MergeCfg<D, G> M;
+    __shared__ float s_red[M::WAVES][G];
+    __shared__ float s_max[G];
+    __shared__ f32x4 s_num[M::SG][M::NE4];
+    __shared__ float s_den[M::SG][G];
+
+    const int t = threadIdx.x;
+    const int e4 = t % M::NE4;
+    const int sg = t / M::NE4;
+    const int h = (e4 * 4) / D;  // query head (within the group) of this float4
     const int hrel = blockIdx.x;  // kv head within the layer range
     const int b = blockIdx.y;
-    const int dim = threadIdx.x;
     const int rel_layer = hrel / a.n_kv_heads;
     const int head = hrel % a.n_kv_heads;
     const int64_t obase =
-        (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)head * G) * D + dim;
+        (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)head * G) * D + e4 * 4;
+
+    auto store = [&](f32x4 o) {
+        if (a.out_bf16) {
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(o.x) | ((uint32_t)f32_to_bf16_rne(o.y) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_rne(o.z) | ((uint32_t)f32_to_bf16_rne(o.w) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + obase) = make_uint2(lo, hi);
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase) = o;
+        }
+    };
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
     const int64_t L = a.ctx_len[b];
-    float o[G];
-    if (fp != a.fingerprint) {
-#pragma unroll
-        for (int h = 0; h < G; h++) o[h] = __builtin_nanf("");
-    } else if (L <= 0) {
-#pragma unroll
-        for (int h = 0; h < G; h++) o[h] = 0.f;
-    } else {
-        const HeadDesc hd = a.heads[a.layer_begin * a.n_kv_heads + hrel];
-        const int64_t n = L < hd.window ? L : hd.window;
-        const int ns = (int)((n + a.split_tokens - 1) / a.split_tokens);
-        const float* rec0 =
-            a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            float M = -INFINITY;
-            for (int s = 0; s < ns; s++) M = fmaxf(M, rec0[(int64_t)s * a.rec_floats + G * D + h]);
-            float num = 0.f, den = 0.f;
-            for (int s = 0; s < ns; s++) {
-                const float* rs = rec0 + (int64_t)s * a.rec_floats;
-                const float f = fast_exp2(rs[G * D + h] - M);
-                num = fmaf(f, rs[h * D + dim], num);
-                den = fmaf(f, rs[G * D + G + h], den);
-            }
-            o[h] = num / den;
+    if (fp != a.fingerprint || L <= 0) {
+        if (sg == 0) {
+            const float x = fp != a.fingerprint ? __builtin_nanf("") : 0.f;
+            store(f32x4{x, x, x, x});
         }
+        return;
+    }
+    const HeadDesc hd = a.heads[a.layer_begin * a.n_kv_heads + hrel];
+    const int64_t n = L < hd.window ? L : hd.window;
+    const int ns = (int)((n + a.split_tokens - 1) / a.split_tokens);
+    const float* rec0 =
+        a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
+
+    // running maxima of the splits, per query head
+    float mloc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) mloc[hh] = -INFINITY;
+    for (int s = t; s < ns; s += M::THREADS) {
+#pragma unroll
+        for (int hh = 0; hh < G; hh++)
+            mloc[hh] = fmaxf(mloc[hh], rec0[(int64_t)s * a.rec_floats + G * D + hh]);
     }
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        if (a.out_bf16)
-            reinterpret_cast<uint16_t*>(a.out)[obase + (int64_t)h * D] = f32_to_bf16_rne(o[h]);
-        else
-            reinterpret_cast<float*>(a.out)[obase + (int64_t)h * D] = o[h];
+    for (int hh = 0; hh < G; hh++) {
+        float x = mloc[hh];
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 8, 64));
+        x = fmaxf(x, __shfl_xor(x, 4, 64));
+        x = fmaxf(x, __shfl_xor(x, 2, 64));
+        x = fmaxf(x, __shfl_xor(x, 1, 64));
+        if ((t & 63) == 0) s_red[t >> 6][hh] = x;
+    }
+    __syncthreads();
+    if (t < G) {
+        float x = s_red[0][t];
+        for (int w = 1; w < M::WAVES; w++) x = fmaxf(x, s_red[w][t]);
+        s_max[t] = x;
+    }
+    __syncthreads();
+
+    const float Mh = s_max[h];
+    const bool den_thread = (e4 * 4) % D == 0;  // first float4 of head h also sums l
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll 4
+    for (int s = sg; s < ns; s += M::SG) {
+        const float* rs = rec0 + (int64_t)s * a.rec_floats;
+        const float f = fast_exp2(rs[G * D + h] - Mh);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(rs + e4 * 4);
+        num.x = fmaf(f, v.x, num.x);
+        num.y = fmaf(f, v.y, num.y);
+        num.z = fmaf(f, v.z, num.z);
+        num.w = fmaf(f, v.w, num.w);
+        if (den_thread) den = fmaf(f, rs[G * D + G + h], den);
+    }
+    s_num[sg][e4] = num;
+    if (den_thread) s_den[sg][h] = den;
+    __syncthreads();
+    if (sg == 0) {
+        f32x4 tot = s_num[0][e4];
+        float dtot = s_den[0][h];
+        for (int k = 1; k < M::SG; k++) {
+            const f32x4 x = s_num[k][e4];
+            tot.x += x.x;
+            tot.y += x.y;
+            tot.z += x.z;
+            tot.w += x.w;
+            dtot += s_den[k][h];
+        }
+        store(f32x4{tot.x / dtot, tot.y / dtot, tot.z / dtot, tot.w / dtot});
     }
 }
 
@@ -436,7 +538,7 @@ hwkv_status launch_split_t(const DecodeSplitArgs& a, hipStream_t s) {
 template <int D, int G>
 hwkv_status launch_merge_t(const DecodeMergeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.n_layers * a.n_kv_heads), (unsigned)a.n_seqs);
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), grid, dim3(D), 0, s, a);
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), grid, dim3(MergeCfg<D, G>::THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(HWKV_ERR_HIP, std::string("decode merge launch: ") + hipGetErrorString(e));

@@ -12,7 +12,7 @@
 namespace hwkv {
 
 constexpr uint32_t kMetaMagic = 0x564B5748u;  // "HWKV"
-constexpr int kDefaultSplitTokens = 512;
+constexpr int kDefaultSplitTokens = 1024;
 constexpr int kMetaAlign = 256;
 
 // Per-head descriptor in the device meta blob (32 bytes, one scalar load).

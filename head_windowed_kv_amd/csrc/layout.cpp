@@ -74,9 +74,9 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
         return fail(HWKV_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) +
                                               " has no kernel (supported: 64, 128)");
     if (split_tokens == 0) split_tokens = kDefaultSplitTokens;
-    if (split_tokens < block_size || split_tokens % block_size != 0 || split_tokens > (1 << 20))
+    if (split_tokens < block_size || split_tokens % block_size != 0 || split_tokens > 2048)
         return fail(HWKV_ERR_INVALID_ARG,
-                    "split_tokens must be a multiple of block_size in [block_size, 2^20]");
+                    "split_tokens must be a multiple of block_size in [block_size, 2048]");
 
     const int64_t n_heads = (int64_t)n_layers * n_kv_heads;
     for (int64_t i = 0; i < n_heads; i++) {

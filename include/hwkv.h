@@ -116,9 +116,9 @@ const char *hwkv_last_error(void);
  * head, each >= 1) -- the per-layer kv_head_windows vectors of the write-up's
  * policy YAML (核心技术 2).  Each head gets nblocks = ceil(w / block_size)
  * blocks.  Supported: block_size 16; head_dim 64 or 128; dtype F32 or BF16.
- * split_tokens is the decode split length S (a multiple of block_size; 0 picks
- * 512).  On success *out owns the layout; free it with hwkv_layout_destroy.
- * Errors: INVALID_ARG (null, n < 1, window < 1), UNSUPPORTED, OVERFLOW. */
+ * split_tokens is the decode split length S (a multiple of block_size, at
+ * most 2048; 0 picks 1024).  On success *out owns the layout; free it with
+ * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1), UNSUPPORTED, OVERFLOW. */
 hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads,
                                const int32_t *windows, int32_t block_size,
                                int32_t head_dim, hwkv_dtype dtype,
