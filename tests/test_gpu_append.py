@@ -16,6 +16,7 @@ def _run_script(windows, dtype, d, n_seqs, table_rows, script, seed, slots=None,
                 layer_begin=0, n_layers=None):
     H = hw()
     dev = device()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     windows = np.asarray(windows, np.int32)
     L_all, n_kv = windows.shape
     n_layers = L_all - layer_begin if n_layers is None else n_layers
@@ -32,8 +33,8 @@ def _run_script(windows, dtype, d, n_seqs, table_rows, script, seed, slots=None,
     slot_t = None if slots is None else torch.tensor(slots, dtype=torch.int32, device=dev)
     for step, (pos0, n_new) in enumerate(script):
         say("append", dtype, d, windows.tolist()[:2], "step", step, "pos0", pos0, "n", n_new)
-        k = synth.randn((n_layers, n_seqs, n_new, n_kv, d), dtype, g)
-        v = synth.randn((n_layers, n_seqs, n_new, n_kv, d), dtype, g)
+        k = synth.randn((n_layers, n_seqs, n_new, n_kv, d), tdt, g)
+        v = synth.randn((n_layers, n_seqs, n_new, n_kv, d), tdt, g)
         p = torch.tensor(pos0, dtype=torch.int64, device=dev)
         H.hwkv_append(cache, layer_begin, n_layers, p, k, v, seq_slots=slot_t)
         oracle.append(ref, ids, windows, 16, d, layer_begin, pos0, synth.to_raw(k),
