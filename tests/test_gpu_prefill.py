@@ -1,0 +1,159 @@
+"""Chunked-prefill parity on the GPU against the fp64 oracle.
+
+Row metric as for decode: max|o - r| / max|r| <= 2e-3 per output row (bf16
+cache, fp32 output).  Covers ragged chunk ends, P = 0 (no history), windows
+shorter and longer than the chunk, all GQA group sizes, d = 64 and 128,
+chunk-size invariance, last row == decode, and the 161K-context
+configuration on sampled rows."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu_common import BF16_TOL, device, hw, row_rel_err, say, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+class PrefillCase:
+    def __init__(self, windows, d, G, pos0, n, seed, hist_keep=None, out_dtype=torch.float32,
+                 split_chunks=None):
+        H = hw()
+        dev = device()
+        self.windows = np.asarray(windows, np.int32)
+        n_kv = self.windows.shape[0]
+        self.n_kv, self.G, self.d, self.n = n_kv, G, d, n
+        self.pos0 = list(pos0)
+        n_seqs = len(pos0)
+        self.lay = H.hwkv_layout_create(self.windows[None, :], 16, d, torch.bfloat16)
+        self.cache = H.make_cache(self.lay, n_seqs, device=dev, fill=0xFF)
+        g = synth.gen(seed, dev)
+        cap = int(((self.windows.astype(np.int64) + 15) // 16 * 16).max())
+        keep = cap if hist_keep is None else hist_keep
+        self.hbase = [max(0, p - keep) for p in pos0]
+        Th = max(max(p - hb for p, hb in zip(pos0, self.hbase)), 1)
+        self.Th = Th
+        self.k_hist = np.zeros((n_seqs, Th, n_kv, d), np.uint16)
+        self.v_hist = np.zeros_like(self.k_hist)
+        for b in range(n_seqs):
+            nh = pos0[b] - self.hbase[b]
+            if nh == 0:
+                continue
+            kh = synth.randn((1, 1, nh, n_kv, d), torch.bfloat16, g)
+            vh = synth.randn((1, 1, nh, n_kv, d), torch.bfloat16, g)
+            self.k_hist[b, :nh] = synth.to_raw(kh[0, 0])
+            self.v_hist[b, :nh] = synth.to_raw(vh[0, 0])
+            H.hwkv_append(self.cache, 0, 1, torch.tensor([self.hbase[b]], device=dev), kh, vh,
+                          seq_slots=torch.tensor([b], dtype=torch.int32, device=dev))
+        self.q = synth.randn((n_seqs, n, n_kv * G, d), torch.bfloat16, g,
+                             std=1.0 / math.sqrt(d))
+        self.k = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+        self.v = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+        torch.cuda.synchronize()
+
+    def run(self, out_dtype=torch.float32, scale=None):
+        H = hw()
+        dev = device()
+        out = torch.full((len(self.pos0), self.n, self.n_kv * self.G, self.d), float("nan"),
+                         dtype=out_dtype, device=dev)
+        s = 1.0 / math.sqrt(self.d) if scale is None else scale
+        H.hwkv_prefill_attn(self.cache, 0, torch.tensor(self.pos0, device=dev), self.q, self.k,
+                            self.v, out, s)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self, rows=None, scale=None):
+        s = 1.0 / math.sqrt(self.d) if scale is None else scale
+        return oracle.prefill(self.windows, self.pos0, synth.to_raw(self.q), synth.to_raw(self.k),
+                              synth.to_raw(self.v), self.k_hist, self.v_hist, self.hbase, s,
+                              rows=rows)
+
+
+def _check(got, ref):
+    assert np.all(np.isfinite(got))
+    err = row_rel_err(got, ref)
+    say("max row rel err", err)
+    assert err <= BF16_TOL, err
+
+
+def test_small_ragged_with_and_without_history():
+    say("prefill small ragged")
+    c = PrefillCase([1, 17, 64, 100], 128, 3, [50, 0], 77, seed=401)
+    _check(to_host_f64(c.run()), c.oracle())
+
+
+@pytest.mark.parametrize("d,G", [(128, 1), (128, 2), (128, 4), (64, 3), (64, 6), (64, 8),
+                                 (128, 8)])
+def test_instances(d, G):
+    say("prefill instance", d, G)
+    c = PrefillCase([33, 700], d, G, [1000, 40, 3], 96, seed=402)
+    _check(to_host_f64(c.run()), c.oracle())
+
+
+def test_windows_longer_than_history_and_chunk_boundaries():
+    # windows reaching past position 0, chunk starting mid-block, long chunk
+    say("prefill long windows")
+    c = PrefillCase([2000, 16, 300, 4096], 128, 3, [123, 1711], 300, seed=403)
+    _check(to_host_f64(c.run()), c.oracle())
+
+
+def test_bf16_output_and_scale():
+    say("prefill bf16 out")
+    c = PrefillCase([64, 130], 128, 2, [500], 64, seed=404)
+    got = to_host_f64(c.run(out_dtype=torch.bfloat16, scale=0.07))
+    ref = c.oracle(scale=0.07)
+    ref_b = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.abs(got - ref_b).max() <= np.abs(ref).max() * 2 ** -7
+
+
+def test_chunk_size_invariance_and_last_row_equals_decode():
+    """Prefill n rows at once == prefill n1, append n1, prefill the rest; the
+    last row equals a decode step at L = P + n after appending the chunk."""
+    H = hw()
+    dev = device()
+    windows = [40, 500, 96]
+    P, n, n1 = 700, 160, 70
+    say("prefill chunk invariance")
+    whole = PrefillCase(windows, 128, 3, [P], n, seed=405)
+    o_all = whole.run()
+    two = PrefillCase(windows, 128, 3, [P], n, seed=405)
+    q, k, v = two.q, two.k, two.v
+    out1 = torch.empty((1, n1, 9, 128), dtype=torch.float32, device=dev)
+    H.hwkv_prefill_attn(two.cache, 0, torch.tensor([P], device=dev), q[:, :n1].contiguous(),
+                        k[:, :n1].contiguous(), v[:, :n1].contiguous(), out1, 1 / math.sqrt(128))
+    H.hwkv_append(two.cache, 0, 1, torch.tensor([P], device=dev), k[None, :, :n1].contiguous(),
+                  v[None, :, :n1].contiguous())
+    out2 = torch.empty((1, n - n1, 9, 128), dtype=torch.float32, device=dev)
+    H.hwkv_prefill_attn(two.cache, 0, torch.tensor([P + n1], device=dev), q[:, n1:].contiguous(),
+                        k[:, n1:].contiguous(), v[:, n1:].contiguous(), out2, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    o_two = torch.cat([out1, out2], dim=1)
+    assert row_rel_err(to_host_f64(o_two), to_host_f64(o_all)) <= 1e-5
+    # decode at L = P + n over the appended chunk, for the last query row
+    H.hwkv_append(two.cache, 0, 1, torch.tensor([P + n1], device=dev),
+                  k[None, :, n1:].contiguous(), v[None, :, n1:].contiguous())
+    ws = H.make_workspace(two.lay, 0, 1, 1, 9, device=dev)
+    dec = torch.empty((1, 1, 9, 128), dtype=torch.float32, device=dev)
+    H.hwkv_decode_attn(two.cache, 0, 1, torch.tensor([P + n], device=dev),
+                       q[None, :, n - 1].contiguous(), 1 / math.sqrt(128), ws, dec)
+    torch.cuda.synchronize()
+    assert row_rel_err(to_host_f64(dec[0, 0]), to_host_f64(o_all[0, n - 1])) <= 1e-5
+
+
+def test_prefill_config_161k_sampled_rows():
+    """4 sequences at 161K context, one 2048-token chunk, windows of the
+    printed policy's layer 0 (up to 65536): sampled rows (first, last, tile
+    and window edges, random) of every head against the oracle."""
+    say("prefill 161K config: fill")
+    c = PrefillCase(list(synth.YAML_LAYER0), 128, 3, [synth.CTX_161K] * 4, 2048, seed=105)
+    say("prefill 161K config: run")
+    got = to_host_f64(c.run())
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 31, 32, 63, 64, 1023, 1024, 2046, 2047] +
+                      list(rng.integers(0, 2048, 14))))
+    say("prefill 161K config: oracle on", len(rows), "rows")
+    ref = c.oracle(rows=rows)
+    _check(got[:, rows], ref)
