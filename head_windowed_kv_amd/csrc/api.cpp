@@ -290,6 +290,7 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a.blocks_per_seq = L->blocks_per_seq;
     a.meta = static_cast<const uint8_t*>(c->meta);
     a.heads = reinterpret_cast<const HeadDesc*>(a.meta + L->heads_off);
+    a.order = reinterpret_cast<const int32_t*>(a.meta + L->order_off);
     a.fingerprint = L->fingerprint;
     a.seq_slots = seq_slots;
     a.pos0 = pos0;

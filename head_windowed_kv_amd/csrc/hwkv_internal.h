@@ -45,6 +45,7 @@ struct MetaHeader {
     uint64_t heads_off;       // byte offset of HeadDesc[n_layers*n_kv_heads]
     uint64_t layer_work_off;  // byte offset of int32[n_layers+1]
     uint64_t work_off;        // byte offset of WorkItem[n_work]
+    uint64_t order_off;       // byte offset of int32[n_layers][n_kv_heads]
 };
 
 }  // namespace hwkv
@@ -65,7 +66,8 @@ struct hwkv_layout {
     std::vector<int32_t> layer_work_off;  // n_layers + 1
     std::vector<hwkv::HeadDesc> heads;
     std::vector<hwkv::WorkItem> work;
-    uint64_t heads_off = 0, layer_work_off_bytes = 0, work_off = 0;
+    std::vector<int32_t> order;  // per layer: kv heads by window, longest first
+    uint64_t heads_off = 0, layer_work_off_bytes = 0, work_off = 0, order_off = 0;
 };
 
 namespace hwkv {
@@ -150,6 +152,7 @@ struct PrefillArgs {
     int64_t blocks_per_seq;
     const uint8_t* meta;
     const HeadDesc* heads;
+    const int32_t* order;  // kv heads of each layer, longest window first
     uint64_t fingerprint;
     const int32_t* seq_slots;
     const int64_t* pos0;

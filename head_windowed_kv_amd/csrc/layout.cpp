@@ -9,6 +9,7 @@
 // the server starts).
 #include <string.h>
 
+#include <algorithm>
 #include <limits>
 #include <new>
 #include <string>
@@ -135,6 +136,14 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
     for (int64_t i = 0; i < n_heads; i++)
         for (int32_t j = 0; j < L->heads[i].max_splits; j++)
             L->work[L->heads[i].work_off + j] = WorkItem{(int32_t)i, j};
+    // prefill schedules the kv heads of a layer longest window first
+    L->order.resize(n_heads);
+    for (int32_t l = 0; l < n_layers; l++) {
+        int32_t* o = L->order.data() + (int64_t)l * n_kv_heads;
+        for (int32_t h = 0; h < n_kv_heads; h++) o[h] = h;
+        const int32_t* wl = windows + (int64_t)l * n_kv_heads;
+        std::stable_sort(o, o + n_kv_heads, [wl](int32_t x, int32_t y) { return wl[x] > wl[y]; });
+    }
 
     uint64_t h = 1469598103934665603ull;
     const uint32_t abi = HWKV_ABI_VERSION;
@@ -152,6 +161,8 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
     off = align_up(off + (uint64_t)(n_layers + 1) * sizeof(int32_t), kMetaAlign);
     L->work_off = off;
     off = align_up(off + (uint64_t)work * sizeof(WorkItem), kMetaAlign);
+    L->order_off = off;
+    off = align_up(off + (uint64_t)n_heads * sizeof(int32_t), kMetaAlign);
     L->meta_bytes = off;
 
     *out = L;
@@ -241,11 +252,13 @@ hwkv_status hwkv_meta_fill(const hwkv_layout* L, void* meta_host, uint64_t meta_
     hdr.heads_off = L->heads_off;
     hdr.layer_work_off = L->layer_work_off_bytes;
     hdr.work_off = L->work_off;
+    hdr.order_off = L->order_off;
     memcpy(base, &hdr, sizeof hdr);
     memcpy(base + L->heads_off, L->heads.data(), L->heads.size() * sizeof(HeadDesc));
     memcpy(base + L->layer_work_off_bytes, L->layer_work_off.data(),
            L->layer_work_off.size() * sizeof(int32_t));
     memcpy(base + L->work_off, L->work.data(), L->work.size() * sizeof(WorkItem));
+    memcpy(base + L->order_off, L->order.data(), L->order.size() * sizeof(int32_t));
     return HWKV_OK;
 }
 
