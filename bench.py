@@ -41,6 +41,11 @@ def parse():
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--config", choices=("stack48", "cb"), default="stack48",
+                   help="stack48: the 48-layer 112K decode step (default, the headline line); "
+                        "cb: the 32-sequence continuous batch, 256 steps (138 GB pool)")
+    p.add_argument("--cb-steps", type=int, default=256)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--counter-pass", action="store_true",
@@ -192,6 +197,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.config == "cb":
+        cb_run(args)
+        return
 
     import numpy as np
     import torch
@@ -323,11 +331,170 @@ def main():
         result["per_layer_graph"] = per_layer_graph(H, torch, cache, lay, windows, q, k_new,
                                                     v_new, L0 + n_steps, n_seqs, n_kv, G, d,
                                                     step_bytes)
+    if not args.no_prefill:
+        del cache, ws  # the decode pool is not needed any more
+        torch.cuda.empty_cache()
+        result["prefill_161k"] = prefill_leg(H, torch, synth)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(windows, L0, n_kv, G, d, args.cpu_seconds,
                                               tok_per_s)
     print(json.dumps(result), flush=True)
+
+
+def cb_run(args):
+    """Continuous batch: 32 sequences with contexts uniform in [4K, 160K],
+    the 48-layer stack's windows, 256 decode steps of append + attention,
+    one launch of each kernel per step for all layers and sequences."""
+    import numpy as np
+    import torch
+
+    import head_windowed_kv_amd as H
+    import synth
+
+    dev = torch.device("cuda", 0)
+    n_layers, n_kv, G, d = 48, 8, 3, 128
+    windows = synth.stack_windows(n_layers, n_kv, 0)
+    L0 = synth.cb_contexts()
+    n_seqs = len(L0)
+    lay = H.hwkv_layout_create(windows, 16, d, torch.bfloat16, args.split_tokens)
+    t = time.time()
+    cache = H.make_cache(lay, n_seqs, device=dev)
+    synth.fill_normal(cache.pool, 104, progress=True)
+    torch.cuda.synchronize()
+    t_fill = time.time() - t
+    g = synth.gen(107, dev)
+    q = synth.randn((n_layers, n_seqs, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+    ws = H.make_workspace(lay, 0, n_layers, n_seqs, n_kv * G, device=dev)
+    out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    L0_t = torch.tensor(L0, dtype=torch.int64, device=dev)
+    n_steps = args.cb_steps
+    kn = synth.randn((n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
+    vn = synth.randn((n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
+    pos = [L0_t + i for i in range(n_steps + 2)]
+    ctx = [L0_t + i + 1 for i in range(n_steps + 2)]
+    scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream()
+
+    def step(i):
+        H.hwkv_append(cache, 0, n_layers, pos[i], kn, vn)
+        H.hwkv_decode_attn(cache, 0, n_layers, ctx[i], q, scale, ws, out)
+
+    step(0)
+    step(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(n_steps):
+        step(2 + i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    w64 = windows.astype(np.int64).reshape(-1)
+    kv_bytes = sum(float(np.minimum(w64[None, :], (L0 + 3 + i)[:, None]).sum())
+                   for i in range(n_steps)) * KV_BYTES_PER_TOK_HEAD
+    res = {"metric": METRIC, "value": round(n_seqs * n_steps / (total_ms / 1e3), 2),
+           "unit": "tokens/s", "n_gpus": 1, "steps": n_steps, "warmup": 2,
+           "ms_per_step": round(total_ms / n_steps, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "continuous_batch_32seq_ctx4k_160k_stack48",
+                      "layers": n_layers, "kv_heads": n_kv, "q_heads": n_kv * G, "head_dim": d,
+                      "block_size": 16, "batch": n_seqs,
+                      "contexts": "uniform integers in [4096, 163840], numpy default_rng(1)",
+                      "split_tokens": lay.desc().split_tokens,
+                      "pool_bytes": cache.pool.numel()},
+           "kv_read_gbps": round(kv_bytes / (total_ms / 1e3) / 1e9, 1),
+           "kv_read_frac_of_peak": round(kv_bytes / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "fill_seconds": round(t_fill, 1)}
+    print(json.dumps(res), flush=True)
+
+
+def prefill_leg(H, torch, synth):
+    """Chunked prefill at 161K context: 4 sequences, 8 KV heads x 3, d=128,
+    bf16, windows of the printed policy's layer 0 (4096 x2, 16384 x2, 65536
+    x4), one 2048-token chunk at P = 164,864; then the chunk is appended and
+    128 decode steps follow.  Prefill attention is timed alone (it only reads
+    the cache, so replays are identical); the append and the decode steps
+    are timed separately."""
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    n_seqs, n_kv, G, d, n = 4, 8, 3, 128, 2048
+    P = synth.CTX_161K
+    w = np.array([synth.YAML_LAYER0], np.int32)
+    lay = H.hwkv_layout_create(w, 16, d, torch.bfloat16)
+    cache = H.make_cache(lay, n_seqs, device=dev)
+    cap = int(((w.astype(np.int64) + 15) // 16 * 16).max())
+    for b in range(n_seqs):  # history: the last `cap` positions before P
+        g = synth.gen(105 * 100003 + b, dev)
+        kh = synth.randn((1, 1, cap, n_kv, d), torch.bfloat16, g)
+        vh = synth.randn((1, 1, cap, n_kv, d), torch.bfloat16, g)
+        H.hwkv_append(cache, 0, 1, torch.tensor([P - cap], device=dev), kh, vh,
+                      seq_slots=torch.tensor([b], dtype=torch.int32, device=dev))
+        del kh, vh
+    g = synth.gen(106, dev)
+    q = synth.randn((n_seqs, n, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+    k = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+    v = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+    out = torch.empty((n_seqs, n, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    pos = torch.full((n_seqs,), P, dtype=torch.int64, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream()
+    for _ in range(2):
+        H.hwkv_prefill_attn(cache, 0, pos, q, k, v, out, scale)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        H.hwkv_prefill_attn(cache, 0, pos, q, k, v, out, scale)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    pf_ms = sorted(ts)[len(ts) // 2]
+    # algorithmic flops: per query row and query head, 4 d flops per key in
+    # its window [p-w+1, p] (QK^T and PV, 2 flops per multiply-add)
+    keys = 0
+    for wh in w[0]:
+        for r in range(n):
+            keys += min(int(wh), P + r + 1)
+    flop = 4.0 * d * G * keys * n_seqs
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    H.hwkv_append(cache, 0, 1, pos, k[None], v[None])
+    e1.record(s)
+    torch.cuda.synchronize()
+    append_ms = e0.elapsed_time(e1)
+    # 128 decode steps after the chunk
+    n_dec = 128
+    kd = synth.randn((n_dec, 1, n_seqs, 1, n_kv, d), torch.bfloat16, g)
+    vd = synth.randn((n_dec, 1, n_seqs, 1, n_kv, d), torch.bfloat16, g)
+    qd = synth.randn((n_dec, 1, n_seqs, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+    posd = [torch.full((n_seqs,), P + n + i, dtype=torch.int64, device=dev) for i in range(n_dec)]
+    ctxd = [torch.full((n_seqs,), P + n + i + 1, dtype=torch.int64, device=dev)
+            for i in range(n_dec)]
+    ws = H.make_workspace(lay, 0, 1, n_seqs, n_kv * G, device=dev)
+    od = torch.empty((1, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(n_dec):
+        H.hwkv_append(cache, 0, 1, posd[i], kd[i], vd[i])
+        H.hwkv_decode_attn(cache, 0, 1, ctxd[i], qd[i].contiguous(), scale, ws, od)
+    e1.record(s)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / n_dec
+    dec_bytes = float(np.minimum(w.astype(np.int64), P + n).sum()) * n_seqs * KV_BYTES_PER_TOK_HEAD
+    return {"workload": "4 seqs x 1 layer, 2048-token chunk at P=164864, windows 4096x2/16384x2/"
+                        "65536x4, 8x3 heads, d=128, bf16",
+            "prefill_ms": round(pf_ms, 4), "prefill_flop": flop,
+            "prefill_tflops": round(flop / (pf_ms / 1e3) / 1e12, 1),
+            "mfma_frac_of_bf16_peak": round(flop / (pf_ms / 1e3) / 2.5e15, 4),
+            "prefill_tokens_per_s": round(n_seqs * n / (pf_ms / 1e3), 1),
+            "chunk_append_ms": round(append_ms, 4),
+            "decode_step_ms": round(dec_ms, 4),
+            "decode_tokens_per_s": round(n_seqs / (dec_ms / 1e3), 1),
+            "decode_kv_read_gbps": round(dec_bytes / (dec_ms / 1e3) / 1e9, 1),
+            "decode_steps": n_dec}
 
 
 def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n_kv, G, d,

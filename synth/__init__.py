@@ -72,3 +72,28 @@ def raw_to_f64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     raise TypeError(a.dtype)
+
+
+def cb_contexts(n_seqs: int = 32, seed: int = 1) -> np.ndarray:
+    """Context lengths of the continuous decode batch: uniform integers in
+    [4K, 160K] from numpy default_rng(seed)."""
+    return np.random.default_rng(seed).integers(4096, 160 * 1024, n_seqs, endpoint=True)
+
+
+def fill_normal(buf_u8: torch.Tensor, seed: int, progress: bool = False) -> None:
+    """Fill a raw byte buffer (a whole KV pool) with N(0,1) bf16 values from
+    torch's generator, in pieces of 2^29 elements (a line per 16 GiB when
+    progress is set)."""
+    import sys
+    import time
+    g = torch.Generator(device=buf_u8.device)
+    g.manual_seed(int(seed))
+    x = buf_u8.view(torch.bfloat16)
+    step = 1 << 29
+    t0 = time.time()
+    for n, i in enumerate(range(0, x.numel(), step)):
+        x[i:i + step].normal_(generator=g)
+        if progress and n % 16 == 15:
+            torch.cuda.synchronize()
+            print("fill: %.0f GiB in %.1f s" % ((i + step) * 2 / 2 ** 30, time.time() - t0),
+                  file=sys.stderr, flush=True)
