@@ -55,18 +55,27 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int D>
 struct PfCfg {
     static constexpr int ROW = D * 2;         // bytes per K or V row (bf16)
-    static constexpr int KS = ROW + 16;       // LDS row stride of the K tile
-    static constexpr int VS = ROW + 64;       // LDS row stride of the V tile
-    static constexpr int KT = kBK * KS;       // bytes of one K tile
-    static constexpr int VT = kBK * VS;       // bytes of one V tile
-    static constexpr int BUF = KT + VT;       // one stage
+    static constexpr int TILE = kBK * ROW;    // bytes of one K or V tile in LDS
     static constexpr int CPR = ROW / 16;      // 16-byte chunks per row
-    static constexpr int CHUNKS = kBK * CPR;  // chunks per K (or V) tile
-    static constexpr int PER_T = CHUNKS / kThreads;
+    static constexpr int RPI = 1024 / ROW;    // rows per LDS-DMA instruction (64 lanes x 16 B)
+    static constexpr int NI = kBS / RPI;      // DMA instructions per 16-key block
     static constexpr int KSTEP = D / 16;      // MFMA k-steps of S^T = K Q^T
     static constexpr int DBLK = D / 32;       // 32-row blocks of O^T
-    static_assert(CHUNKS % kThreads == 0, "tile chunks must divide evenly");
+    static_assert(kWaves * kBS == kBK, "each wave stages one 16-key block of a tile");
 };
+
+// LDS tiles are unpadded; the 16-byte chunks of a row are permuted by an XOR
+// with a function of the row so that the MFMA operand reads hit distinct
+// banks: the K reads take one chunk of 16 consecutive rows, the transposed V
+// reads 32 bytes of 4 consecutive rows.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 2 * ((2 * (r & 3)) ^ ((r >> 1) & 1)) : 2 * (r & 3);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -80,20 +89,37 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-// Four consecutive bf16 of row (k0 + j/4), columns n0 + 4(j%4) .. +3, read by
-// lane j of a 16-lane group; the transpose read hands lane i of the group the
-// four rows' elements of column n0 + i.
-__device__ __forceinline__ u32x2 tr_read(const uint8_t* lds_v, int row, int col, int vs) {
-    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(lds_v + row * vs + col * 2));
+// Four consecutive bf16 at byte address `addr` of the V tile, read by lane j
+// of a 16-lane group; the transpose read hands lane i of the group the four
+// rows' elements of one column.
+__device__ __forceinline__ u32x2 tr_read(const uint8_t* addr) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
     return __builtin_bit_cast(u32x2, r);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes lds + 16 i
+// (the LDS address is the same for the whole wave).  A dword at or beyond the
+// resource's byte count reads as zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     typedef PfCfg<D> C;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // two stages of K and V tiles; separate objects so that the compiler sees
+    // that a DMA into one stage never aliases the reads of the other
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TILE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -139,64 +165,73 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int64_t pmax_q = P + (int64_t)pb_max * kQW + kQW - 1;
     const int64_t pmax = pmax_q < P + n - 1 ? pmax_q : P + n - 1;
     const int64_t kmin = pmin - w + 1 > 0 ? pmin - w + 1 : 0;
-    const int64_t kmax = pmax;
     const int64_t T0 = kmin / kBK;
-    const int n_tiles = (int)(kmax / kBK - T0 + 1);
-    // key range of this wave
+    const int n_tiles = (int)(pmax / kBK - T0 + 1);
     const int64_t wq_last = p0 + kQW - 1 < P + n - 1 ? p0 + kQW - 1 : P + n - 1;
-    const int64_t wk_lo = p0 - w + 1 > 0 ? p0 - w + 1 : 0;
-    const int64_t wk_hi = wq_last;
 
     const int32_t* tbl = a.block_ids + (seq_ok ? slot : 0) * a.blocks_per_seq + hd.table_off;
-    const uint32_t nb = (uint32_t)hd.nblocks;
-    const int64_t kv_row_stride = (int64_t)a.n_kv_heads * D * 2;  // bytes between chunk rows
-    const uint8_t* kc_base = a.k + ((int64_t)b * n * a.n_kv_heads + kvh) * D * 2;
-    const uint8_t* vc_base = a.v + ((int64_t)b * n * a.n_kv_heads + kvh) * D * 2;
+    const const_i32* tblc = (const const_i32*)tbl;
+    const int32_t nb = hd.nblocks;
+    const int64_t stride = (int64_t)a.n_kv_heads * C::ROW;  // bytes between chunk rows
+    const uint8_t* kc_base = a.k + ((int64_t)b * n * a.n_kv_heads + kvh) * C::ROW;
+    const uint8_t* vc_base = a.v + ((int64_t)b * n * a.n_kv_heads + kvh) * C::ROW;
 
-    // ---- tile staging: 4 threads per key row, each a quarter of the row ----
-    constexpr int QB = C::ROW / 4;  // bytes per quarter row
-    constexpr int NQ = QB / 16;     // 16-byte chunks per quarter row
-    const int lkey = threadIdx.x >> 2;
-    const int lq = threadIdx.x & 3;
-    u32x4 stK[NQ], stV[NQ];
-    // ring block of the first block of the current tile, advanced by 4 per tile
-    uint32_t jt = (uint32_t)((T0 * (kBK / kBS)) % nb);
-    // Every thread loads unconditionally: a key outside [kmin, kmax] (needed by
-    // no query of the workgroup, its score is masked) is read from the
-    // clamped position instead, and an id outside the pool from block 0, so
-    // all addresses are valid and all data finite for valid caches.  The
-    // block id of a tile is fetched one tile ahead of its K/V rows.
-    auto key_of = [&](int64_t T) {
-        const int64_t t = T * kBK + lkey;
-        return t < kmin ? kmin : (t > kmax ? kmax : t);
-    };
-    auto fetch_id = [&](int64_t T, uint32_t j_first) -> int32_t {
-        const int64_t t = key_of(T);
-        uint32_t j = j_first + (uint32_t)((t - T * kBK) / kBS);
-        while (j >= nb) j -= nb;
-        return tbl[t < P ? j : 0];
-    };
-    auto load_tile = [&](int64_t T, int32_t id) {
-        const int64_t t = key_of(T);
-        const bool hist = t < P;
-        const uint64_t idc = (id >= 0 && (uint64_t)id < a.n_pool_blocks) ? (uint64_t)id : 0;
-        const uint8_t* kp = hist ? a.pool + idc * a.block_bytes + (t % kBS) * C::ROW
-                                 : kc_base + (t - P) * kv_row_stride;
-        const uint8_t* vp = hist ? kp + kBS * C::ROW : vc_base + (t - P) * kv_row_stride;
+    // ---- staging: wave w moves the 16-key block w of every tile ----
+    // DMA instruction j of a wave fills LDS rows RPI j .. RPI j + RPI - 1 of
+    // the block; lane i writes LDS chunk i % CPR of row RPI j + i / CPR, so it
+    // fetches the global chunk that the row's swizzle puts there.
+    const int lq = lane / C::CPR, la = lane % C::CPR;
+    const uint32_t ck = (uint32_t)((la ^ swz_k<D>(lq)) * 16);
+    const uint32_t cv = (uint32_t)((la ^ swz_v<D>(lq)) * 16);
+    const uint32_t hK = (uint32_t)(lq * C::ROW) + ck, hV = (uint32_t)(lq * C::ROW) + cv;
+    const uint32_t cK = (uint32_t)(lq * stride) + ck, cV = (uint32_t)(lq * stride) + cv;
+    // the K swizzle of row RPI j + lq differs from that of row lq by xk(j)
+    auto xk = [](int j) -> uint32_t { return (uint32_t)((swz_k<D>(C::RPI * j) ) * 16); };
+    const int64_t pool_blocks = (int64_t)a.n_pool_blocks;
+
+    auto issue = [&](uint8_t* slot_base, int64_t X, int32_t id, bool is_v) {
+        uint8_t* dst = slot_base + wave * (kBS * C::ROW);
+        const int64_t tb = X * kBK + wave * kBS;  // first key of the block
+        const int64_t idc = (id >= 0 && id < pool_blocks) ? id : 0;
+        const rsrc_t rh = make_rsrc(a.pool + idc * a.block_bytes + (is_v ? kBS * C::ROW : 0),
+                                    kBS * C::ROW);
+        const uint8_t* cbase = is_v ? vc_base : kc_base;
+        if (tb + kBS <= P) {  // history block: every row from the ring block
 #pragma unroll
-        for (int i = 0; i < NQ; i++) {
-            stK[i] = *reinterpret_cast<const u32x4*>(kp + lq * QB + i * 16);
-            stV[i] = *reinterpret_cast<const u32x4*>(vp + lq * QB + i * 16);
+            for (int j = 0; j < C::NI; j++)
+                dma16(rh, is_v ? hV : (hK ^ xk(j)), j * 1024, dst + j * 1024);
+        } else if (tb >= P) {
+            // rows of the chunk's own k, v; rows past the chunk end read as
+            // zero (no query attends to them)
+            // (a block wholly past the end gets an empty range)
+            const int64_t r0 = tb - P;
+            const int64_t rows = n - r0 < kBS ? (n - r0 > 0 ? n - r0 : 0) : kBS;
+            const rsrc_t rc = make_rsrc(cbase + r0 * stride, (uint32_t)(rows * stride));
+#pragma unroll
+            for (int j = 0; j < C::NI; j++)
+                dma16(rc, (uint32_t)(j * C::RPI * stride) + (is_v ? cV : (cK ^ xk(j))), 0,
+                      dst + j * 1024);
+        } else {
+            // the block that holds the chunk start: rows before it from the
+            // ring block, rows from it on from the chunk
+            const rsrc_t rc = make_rsrc(cbase, (uint32_t)((n < kBS ? n : kBS) * stride));
+#pragma unroll
+            for (int j = 0; j < C::NI; j++) {
+                const int64_t t = tb + C::RPI * j + lq;
+                const uint32_t cpart = is_v ? cv : (ck ^ xk(j));
+                if (t < P)
+                    dma16(rh, is_v ? hV : (hK ^ xk(j)), j * 1024, dst + j * 1024);
+                else
+                    dma16(rc, (uint32_t)((t - P) * stride) + cpart, 0, dst + j * 1024);
+            }
         }
     };
-    auto store_tile = [&](int buf) {
-        uint8_t* kb = smem + buf * C::BUF;
-        uint8_t* vb = kb + C::KT;
-#pragma unroll
-        for (int i = 0; i < NQ; i++) {
-            *reinterpret_cast<u32x4*>(kb + lkey * C::KS + lq * QB + i * 16) = stK[i];
-            *reinterpret_cast<u32x4*>(vb + lkey * C::VS + lq * QB + i * 16) = stV[i];
-        }
+    int32_t jw = (int32_t)((T0 * (kBK / kBS) + wave) % nb);  // ring block of the next id
+    auto next_id = [&]() -> int32_t {
+        const int32_t id = tblc[jw];
+        jw += kBK / kBS;
+        while (jw >= nb) jw -= nb;
+        return id;
     };
 
     // ---- Q^T operands of this wave (query col, head qg): 16 dims per k-step ----
@@ -212,147 +247,172 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                          : u32x4{0, 0, 0, 0};
     }
 
+    // K operand of k-step s for key row 32 kb2 + col: chunk 2 s + h2 of the row
+    const uint32_t kx = (uint32_t)(col * C::ROW) + (uint32_t)((h2 ^ swz_k<D>(col)) * 16);
+    // V^T operands: lane group g16 = lane/16 covers d columns 16 (g16 & 1)
+    // (+32 db) and key offsets 4 (g16 >> 1) and 8 + 4 (g16 >> 1) inside each
+    // 16-key step; lane j16 of the group reads row j16/4, columns 4 (j16 % 4)
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int rrow = j16 >> 2, rc = j16 & 3;
+    uint32_t vaddr[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; db++) {
+        const int c16 = db * 4 + (g16 & 1) * 2 + (rc >> 1);
+        vaddr[db] = (uint32_t)(((g16 >> 1) * 4 + rrow) * C::ROW) +
+                    (uint32_t)((c16 ^ swz_v<D>(rrow)) * 16) + (uint32_t)((rc & 1) * 8);
+    }
+
+    auto qk = [&](const uint8_t* kt, f32x16& s0, f32x16& s1) {
+        s0 = f32x16{};
+        s1 = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::KSTEP; s++) {
+            const uint32_t off = kx ^ (uint32_t)(32 * s);
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + off);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + 32 * C::ROW + off);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qop[s]), s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qop[s]), s1, 0, 0, 0);
+        }
+    };
+
+    // mask keys outside [pq-w+1, pq] (with u = pq - t, keep 0 <= u < w) and
+    // return the tile maximum in the log2 domain
+    const float c2 = a.qk_scale_log2;
+    auto mask_max = [&](f32x16* sc, int64_t X) -> float {
+        const int64_t kt0 = X * kBK;
+        const bool full = kt0 >= wq_last - w + 1 && kt0 + kBK - 1 <= p0;
+        if (!full) {
+            const int32_t ubase = col - (int32_t)(kt0 - p0) - h2 * 4;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int32_t uu = ubase - (kb2 * 32 + (r >> 2) * 8 + (r & 3));
+                    if (!((uint32_t)uu < (uint32_t)w)) sc[kb2][r] = -INFINITY;
+                }
+        }
+        float m8[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            m8[i] = fmaxf(fmaxf(sc[i >> 2][4 * (i & 3)], sc[i >> 2][4 * (i & 3) + 1]),
+                          fmaxf(sc[i >> 2][4 * (i & 3) + 2], sc[i >> 2][4 * (i & 3) + 3]));
+        const float mt = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                               fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        return fmaxf(mt, xor32f(mt)) * c2;
+    };
+
     f32x16 oacc[C::DBLK];
 #pragma unroll
     for (int db = 0; db < C::DBLK; db++) oacc[db] = f32x16{};
     // running max in the log2 domain; it is only raised when some lane's tile
     // maximum exceeds it by more than kLazy, so P stays below 2^kLazy
     float m_run = kEmptyMax, l_run = 0.f;
-    const float c2 = a.qk_scale_log2;
 
-    // jt: ring block of the first block of tile T0 + it + 1 (advanced by 4 per tile)
-    int32_t id_next = 0;
+    // P = 2^(s c2 - m) of k-step ks (keys 16 ks .. 16 ks + 15) as B operands:
+    // high part = P truncated to bf16, low part = the exact remainder rounded
+    // to bf16; psum collects the fp32 P values
+    auto make_p = [&](const f32x16* sc, int ks, u32x4& hi, u32x4& lo, float& psum) {
+        const int kb2 = ks >> 1, half = ks & 1;
+        uint32_t hw[4], lw[4];
+        float ps[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int r0 = (e < 2 ? 2 * half : 2 * half + 1) * 4 + (e & 1) * 2;
+            const float pa = fast_exp2(fmaf(sc[kb2][r0], c2, -m_run));
+            const float pb2 = fast_exp2(fmaf(sc[kb2][r0 + 1], c2, -m_run));
+            const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb2);
+            hw[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+            lw[e] = pack_bf16(pa - __uint_as_float(ua & 0xffff0000u),
+                              pb2 - __uint_as_float(ub & 0xffff0000u));
+            ps[e] = pa + pb2;
+        }
+        hi = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        lo = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        psum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+
+    // O^T += V^T P^T for k-step ks; the V^T operands come from transpose reads
+    auto pv = [&](const uint8_t* vt, int ks, const u32x4& hi, const u32x4& lo) {
+        const int roff = ((ks >> 1) * 32 + (ks & 1) * 16) * C::ROW;
+        bf16x8 va[C::DBLK];
+#pragma unroll
+        for (int db = 0; db < C::DBLK; db++) {
+            const u32x2 r0 = tr_read(vt + roff + vaddr[db]);
+            const u32x2 r1 = tr_read(vt + roff + 8 * C::ROW + vaddr[db]);
+            va[db] = as_bf16x8(u32x4{r0.x, r0.y, r1.x, r1.y});
+        }
+#pragma unroll
+        for (int db = 0; db < C::DBLK; db++)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(hi), oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < C::DBLK; db++)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(lo), oacc[db], 0, 0, 0);
+    };
+
+    // ---- software pipeline over key tiles ----
+    // Iteration it (tile T = T0 + it) finds S^T of T in registers and K of
+    // T + 1, V of T in LDS; it starts the DMA of K of T + 2 and V of T + 1,
+    // computes S^T of T + 1 while it exponentiates T, and multiplies P of T
+    // into O while it finishes the exponentials and masks T + 1.
+    f32x16 sA[2], sB[2];  // S^T of the current and of the next tile, alternating
+    float mt = kEmptyMax;
+    int32_t idK = 0, idV = 0;
     if (n_tiles > 0) {
-        load_tile(T0, fetch_id(T0, jt));
-        store_tile(0);
-        jt += kBK / kBS;
-        while (jt >= nb) jt -= nb;
-        if (n_tiles > 1) id_next = fetch_id(T0 + 1, jt);
+        const int32_t id0 = next_id();
+        issue(sK0, T0, id0, false);
+        issue(sV0, T0, id0, true);
+        const int32_t id1 = next_id();
+        if (n_tiles > 1) issue(sK1, T0 + 1, id1, false);
+        idV = id1;
+        idK = next_id();
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    __builtin_amdgcn_s_waitcnt(0);  // nothing loaded before the loop is pending in it
-    for (int it = 0; it < n_tiles; it++) {
+    if (wave_on && n_tiles > 0) {
+        qk(sK0, sA[0], sA[1]);
+        mt = mask_max(sA, T0);
+    }
+
+    auto step = [&](int it, const uint8_t* k_rd, const uint8_t* v_rd, uint8_t* k_dma, uint8_t* v_dma,
+                    f32x16* s_cur, f32x16* s_next) {
         const int64_t T = T0 + it;
-        const int cur = it & 1;
-        const bool more = it + 1 < n_tiles;
-        if (more) {
-            load_tile(T + 1, id_next);
-            if (it + 2 < n_tiles) {
-                jt += kBK / kBS;
-                while (jt >= nb) jt -= nb;
-                id_next = fetch_id(T + 2, jt);
-            }
-        }
-        const int64_t kt0 = T * kBK;
-        const bool touch = wave_on && kt0 + kBK - 1 >= wk_lo && kt0 <= wk_hi;
-        if (touch) {
-            const uint8_t* kb = smem + cur * C::BUF;
-            const uint8_t* vb = kb + C::KT;
-            // S^T for the two 32-key halves of the tile
-            // The two 32-key halves are independent accumulation chains; their
-            // MFMAs alternate and each K operand is read two steps ahead.
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            {
-                const uint8_t* krow0 = kb + col * C::KS + h2 * 16;
-                const uint8_t* krow1 = krow0 + 32 * C::KS;
-                u32x4 ka0[C::KSTEP], ka1[C::KSTEP];
-#pragma unroll
-                for (int s = 0; s < C::KSTEP; s++) {
-                    ka0[s] = *reinterpret_cast<const u32x4*>(krow0 + s * 32);
-                    ka1[s] = *reinterpret_cast<const u32x4*>(krow1 + s * 32);
-                }
-#pragma unroll
-                for (int s = 0; s < C::KSTEP; s++) {
-                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(ka0[s]), as_bf16x8(qop[s]), sacc[0], 0, 0, 0);
-                    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(ka1[s]), as_bf16x8(qop[s]), sacc[1], 0, 0, 0);
-                }
-                // order: 4 reads, then (2 reads, 2 MFMAs) per step
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-                for (int s = 0; s < C::KSTEP - 2; s++) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            }
-            // mask keys outside [pq-w+1, pq]: with u = pq - t, keep 0 <= u < w
-            const bool full = kt0 >= wq_last - w + 1 && kt0 + kBK - 1 <= p0;
-            if (!full) {
-                const int32_t ubase = col - (int32_t)(kt0 - p0) - h2 * 4;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; kb2++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int32_t uu = ubase - (kb2 * 32 + (r >> 2) * 8 + (r & 3));
-                        if (!((uint32_t)uu < (uint32_t)w)) sacc[kb2][r] = -INFINITY;
-                    }
-            }
-            float mt = -INFINITY;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; kb2++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) mt = fmaxf(mt, sacc[kb2][r]);
-            mt = fmaxf(mt, xor32f(mt)) * c2;
-            if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
-                const float m_new = fmaxf(m_run, mt);
-                const float alpha = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < C::DBLK; db++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) oacc[db][r] *= alpha;
-            }
-            // P = 2^(s c2 - m) as B operands: high part = P truncated to bf16,
-            // low part = the exact remainder rounded to bf16
-            u32x4 phi[4], plo[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const int kb2 = ks >> 1, half = ks & 1;
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r0 = (e < 2 ? 2 * half : 2 * half + 1) * 4 + (e & 1) * 2;
-                    const float pa = fast_exp2(fmaf(sacc[kb2][r0], c2, -m_run));
-                    const float pb2 = fast_exp2(fmaf(sacc[kb2][r0 + 1], c2, -m_run));
-                    const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb2);
-                    hw[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-                    lw[e] = pack_bf16(pa - __uint_as_float(ua & 0xffff0000u),
-                                      pb2 - __uint_as_float(ub & 0xffff0000u));
-                    l_run += pa + pb2;
-                }
-                phi[ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-                plo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            }
-            // O^T += V^T P^T; V^T operands by transpose reads.  Lane group
-            // g16 = lane/16 covers d columns 16*(g16&1) (+32 db) and key
-            // offsets 4*(g16>>1) and 8 + 4*(g16>>1) inside each 16-key step.
-            const int g16 = lane >> 4, j16 = lane & 15;
-            const int rrow = j16 >> 2, rcol = (j16 & 3) * 4;
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const int kbase = (ks >> 1) * 32 + (ks & 1) * 16 + (g16 >> 1) * 4;
-                bf16x8 va[C::DBLK];  // this k-step's V^T operands, read before the MFMAs
-#pragma unroll
-                for (int db = 0; db < C::DBLK; db++) {
-                    const int dcol = db * 32 + (g16 & 1) * 16 + rcol;
-                    const u32x2 r0 = tr_read(vb, kbase + rrow, dcol, C::VS);
-                    const u32x2 r1 = tr_read(vb, kbase + 8 + rrow, dcol, C::VS);
-                    va[db] = as_bf16x8(u32x4{r0.x, r0.y, r1.x, r1.y});
-                }
-#pragma unroll
-                for (int db = 0; db < C::DBLK; db++) {
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(phi[ks]),
-                                                                       oacc[db], 0, 0, 0);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(plo[ks]),
-                                                                       oacc[db], 0, 0, 0);
-                }
-            }
-        }
-        if (more) store_tile(cur ^ 1);
+        // K of T + 1 and V of T have landed (the wait covers this wave's LDS
+        // DMA, which the compiler does not track); K of T, V of T - 1 are free
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
+        if (it + 1 < n_tiles) issue(v_dma, T + 1, idV, true);
+        idV = idK;
+        idK = next_id();
+        if (!wave_on) return;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DBLK; db++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) oacc[db][r] *= alpha;
+        }
+        u32x4 phi[4], plo[4];
+        float psum = 0.f;
+        qk(k_rd, s_next[0], s_next[1]);
+        make_p(s_cur, 0, phi[0], plo[0], psum);
+        make_p(s_cur, 1, phi[1], plo[1], psum);
+        pv(v_rd, 0, phi[0], plo[0]);
+        pv(v_rd, 1, phi[1], plo[1]);
+        make_p(s_cur, 2, phi[2], plo[2], psum);
+        make_p(s_cur, 3, phi[3], plo[3], psum);
+        pv(v_rd, 2, phi[2], plo[2]);
+        pv(v_rd, 3, phi[3], plo[3]);
+        l_run += psum;
+        if (it + 1 < n_tiles) mt = mask_max(s_next, T + 1);
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        step(it, sK1, sV0, sK0, sV1, sA, sB);
+        if (it + 1 >= n_tiles) break;
+        step(it + 1, sK0, sV1, sK1, sV0, sB, sA);
     }
 
     // ---- normalise and write this lane's query row ----
@@ -379,7 +439,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
 template <int D, int G>
 hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
-    typedef PfCfg<D> C;
     const int n_pb = (a.n_chunk + kQW - 1) / kQW;
     const int n_units = G * n_pb;
     const int64_t n_groups = (n_units + kWaves - 1) / kWaves;
@@ -387,13 +446,8 @@ hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
     const int64_t blocks = (n_pairs + kXcds - 1) / kXcds * kXcds * n_groups;
     if (blocks > 0x7fffffff) return fail(HWKV_ERR_OVERFLOW, "prefill grid too large");
     dim3 grid((unsigned)blocks);
-    const size_t lds = 2 * (size_t)C::BUF;  // two K/V stages, above the 64 KiB default
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess)
-        return fail(HWKV_ERR_HIP, std::string("prefill LDS attribute: ") + hipGetErrorString(e));
-    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), lds, s, a);
-    e = hipGetLastError();
+    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(HWKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
     return HWKV_OK;
