@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--graph-split-tokens", type=int, default=256,
+                   help="decode split length of the second per-layer graph variant")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--config", choices=("stack48", "cb"), default="stack48",
                    help="stack48: the 48-layer 112K decode step (default, the headline line); "
@@ -327,10 +329,18 @@ def main():
     result["practical_read_ceiling_gbps"] = round(ceiling, 1)
     result["roofline"]["frac_of_practical_ceiling"] = round(split_gbps / ceiling, 4)
 
+    result["single_launch_step"] = fused_leg(H, torch, cache, lay, q, k_new, v_new,
+                                             L0 + n_steps, n_seqs, n_kv, G, d, args.steps,
+                                             step_bytes)
     if not args.no_graph:
-        result["per_layer_graph"] = per_layer_graph(H, torch, cache, lay, windows, q, k_new,
-                                                    v_new, L0 + n_steps, n_seqs, n_kv, G, d,
-                                                    step_bytes)
+        for fused in (False, True):
+            for st in (desc.split_tokens, args.graph_split_tokens):
+                key = "per_layer_graph%s_split%d" % ("_single_launch" if fused else "", st)
+                glay = lay if st == desc.split_tokens else \
+                    H.hwkv_layout_create(windows, bs, d, torch.bfloat16, st)
+                result[key] = per_layer_graph(H, torch, cache, glay, windows, q, k_new, v_new,
+                                              L0 + n_steps + 64, n_seqs, n_kv, G, d, step_bytes,
+                                              fused)
     if not args.no_prefill:
         del cache, ws  # the decode pool is not needed any more
         torch.cuda.empty_cache()
@@ -498,16 +508,25 @@ def prefill_leg(H, torch, synth):
 
 
 def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n_kv, G, d,
-                    step_bytes):
+                    step_bytes, fused=False):
     """The model-realistic launch pattern: per layer append -> split -> merge
     (each layer's q only exists after the previous layer), 144 launches
     captured once in a HIP graph and replayed; positions live in device
-    scalars updated by a fill kernel outside the graph."""
+    scalars updated by a fill kernel outside the graph.  fused: one
+    hwkv_decode_step launch per layer instead (48 launches).  `lay` may
+    differ from the cache's layout in its decode split length only (same
+    windows, so the same pool geometry); its own meta blob is used."""
     dev = q.device
     n_layers = windows.shape[0]
+    if lay is not cache.layout:
+        meta_host = H.hwkv_meta_fill(lay)
+        meta = H._alloc_aligned(meta_host.size, dev)
+        meta.copy_(torch.from_numpy(meta_host))
+        cache = H.Cache(lay, cache.pool, cache.block_ids, meta)
     pos = torch.full((n_seqs,), L, dtype=torch.int64, device=dev)
     ctx = torch.full((n_seqs,), L + 1, dtype=torch.int64, device=dev)
-    wss = [H.make_workspace(lay, l, 1, n_seqs, n_kv * G, device=dev) for l in range(n_layers)]
+    mk = H.make_step_workspace if fused else H.make_workspace
+    wss = [mk(lay, l, 1, n_seqs, n_kv * G, device=dev) for l in range(n_layers)]
     out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
     kn = k_new[0].clone()
     vn = v_new[0].clone()
@@ -519,15 +538,20 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        for l in range(n_layers):  # warm the launch path once, eagerly
+    def layer_step(l):
+        if fused:
+            H.hwkv_decode_step(cache, l, 1, pos, kns[l], vns[l], qs[l], scale, wss[l], outs[l])
+        else:
             H.hwkv_append(cache, l, 1, pos, kns[l], vns[l])
             H.hwkv_decode_attn(cache, l, 1, ctx, qs[l], scale, wss[l], outs[l])
+
+    with torch.cuda.stream(side):
+        for l in range(n_layers):  # warm the launch path once, eagerly
+            layer_step(l)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=side):
             for l in range(n_layers):
-                H.hwkv_append(cache, l, 1, pos, kns[l], vns[l])
-                H.hwkv_decode_attn(cache, l, 1, ctx, qs[l], scale, wss[l], outs[l])
+                layer_step(l)
     torch.cuda.synchronize()
     n_rep = 20
     s = torch.cuda.current_stream()
@@ -547,7 +571,38 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
     b = step_bytes(L + 2)
     return {"ms_per_step_median": round(ms, 4), "tokens_per_s": round(n_seqs / (ms / 1e3), 2),
             "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
-            "launches_per_step": 3 * n_layers, "replays": n_rep}
+            "launches_per_step": (1 if fused else 3) * n_layers, "replays": n_rep,
+            "split_tokens": lay.desc().split_tokens}
+
+
+def fused_leg(H, torch, cache, lay, q, k_new, v_new, L, n_seqs, n_kv, G, d, steps, step_bytes):
+    """The same decode step as one hwkv_decode_step launch for all 48 layers
+    (append, split and merge fused), timed with HIP events over `steps`
+    consecutive steps that continue the token stream."""
+    dev = q.device
+    n_layers = q.shape[0]
+    ws = H.make_step_workspace(lay, 0, n_layers, n_seqs, n_kv * G, device=dev)
+    out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    pos = [torch.full((n_seqs,), L + i, dtype=torch.int64, device=dev) for i in range(steps + 3)]
+    scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream()
+    for i in range(3):
+        H.hwkv_decode_step(cache, 0, n_layers, pos[i], k_new[i % len(k_new)],
+                           v_new[i % len(v_new)], q, scale, ws, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(steps):
+        H.hwkv_decode_step(cache, 0, n_layers, pos[3 + i], k_new[i % len(k_new)],
+                           v_new[i % len(v_new)], q, scale, ws, out)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    b = step_bytes(L + 3)
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(n_seqs / (ms / 1e3), 2),
+            "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
+            "kv_read_frac_of_peak": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "launches_per_step": 1, "steps": steps}
 
 
 def cpu_baseline(windows, L, n_kv, G, d, target_s, gpu_tok_s):

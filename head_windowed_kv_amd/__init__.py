@@ -38,7 +38,8 @@ STATUS_NAMES = {0: "HWKV_OK", 1: "HWKV_ERR_INVALID_ARG", 2: "HWKV_ERR_UNSUPPORTE
 EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_layout_destroy",
             "hwkv_layout_query", "hwkv_mem_estimate", "hwkv_table_fill", "hwkv_meta_fill",
             "hwkv_workspace_bytes", "hwkv_append", "hwkv_decode_split", "hwkv_decode_merge",
-            "hwkv_decode_attn", "hwkv_prefill_attn")
+            "hwkv_decode_attn", "hwkv_step_workspace_bytes", "hwkv_decode_step",
+            "hwkv_prefill_attn")
 
 
 class hwkv_layout_desc(ctypes.Structure):
@@ -91,6 +92,11 @@ _lib.hwkv_decode_merge.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _
 _lib.hwkv_decode_attn.restype = ctypes.c_int
 _lib.hwkv_decode_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _i32, _vp,
                                   _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
+_lib.hwkv_step_workspace_bytes.restype = ctypes.c_int
+_lib.hwkv_step_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _i32, _P(_u64)]
+_lib.hwkv_decode_step.restype = ctypes.c_int
+_lib.hwkv_decode_step.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                  _i32, _vp, _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
 _lib.hwkv_prefill_attn.restype = ctypes.c_int
 _lib.hwkv_prefill_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _vp, _vp, _i32, _i32, _vp,
                                    _vp, _vp, _vp, ctypes.c_int, _f32, _vp]
@@ -260,6 +266,24 @@ def make_workspace(layout: Layout, layer_begin: int, n_layers: int, n_seqs: int,
                                                    n_q_heads), 256), device)
 
 
+def hwkv_step_workspace_bytes(layout: Layout, layer_begin: int, n_layers: int, n_seqs: int,
+                              n_q_heads: int) -> int:
+    b = ctypes.c_uint64()
+    _check(_lib.hwkv_step_workspace_bytes(layout.handle, layer_begin, n_layers, n_seqs,
+                                          n_q_heads, ctypes.byref(b)))
+    return int(b.value)
+
+
+def make_step_workspace(layout: Layout, layer_begin: int, n_layers: int, n_seqs: int,
+                        n_q_heads: int, device="cuda") -> torch.Tensor:
+    """Workspace of hwkv_decode_step, zero-filled once (its arrival counters
+    must start at zero; every call leaves them at zero)."""
+    ws = _alloc_aligned(hwkv_step_workspace_bytes(layout, layer_begin, n_layers, n_seqs,
+                                                  n_q_heads), device)
+    ws.zero_()
+    return ws
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -350,6 +374,34 @@ def hwkv_decode_attn(cache: Cache, layer_begin: int, n_layers: int, ctx_len: tor
                                  int(q.shape[1]), _ptr(seq_slots), _ptr(ctx_len), int(q.shape[2]),
                                  _ptr(q), scale, _ptr(workspace), workspace.numel(), _ptr(out),
                                  _dtype_code(out.dtype), _stream(stream)))
+
+
+def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,
+                     k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, scale: float,
+                     workspace: torch.Tensor, out: torch.Tensor,
+                     seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append of the token at position pos[b] and decode at context pos[b]+1
+    in one launch.  k_new, v_new: [n_layers][n_seqs][n_kv_heads][head_dim] (or
+    with a unit token axis [n_layers][n_seqs][1][n_kv_heads][head_dim]);
+    q, out: [n_layers][n_seqs][n_q_heads][head_dim]."""
+    d = cache.layout.desc()
+    n_seqs, n_q = int(q.shape[1]), int(q.shape[2])
+    _expect("q", q, (n_layers, n_seqs, n_q, d.head_dim), torch_dtype(d.dtype))
+    kv_shape = (n_layers, n_seqs, d.n_kv_heads, d.head_dim)
+    if k_new.dim() == 5:
+        kv_shape = (n_layers, n_seqs, 1, d.n_kv_heads, d.head_dim)
+    _expect("k_new", k_new, kv_shape, torch_dtype(d.dtype))
+    _expect("v_new", v_new, kv_shape, torch_dtype(d.dtype))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out must be float32 or bfloat16")
+    _expect("out", out, tuple(q.shape), out.dtype)
+    _expect("pos", pos, (n_seqs,), torch.int64)
+    _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
+    cv = cache.view()
+    _check(_lib.hwkv_decode_step(cache.layout.handle, ctypes.byref(cv), layer_begin, n_layers,
+                                 n_seqs, _ptr(seq_slots), _ptr(pos), _ptr(k_new), _ptr(v_new),
+                                 n_q, _ptr(q), scale, _ptr(workspace), workspace.numel(),
+                                 _ptr(out), _dtype_code(out.dtype), _stream(stream)))
 
 
 def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,

@@ -259,6 +259,40 @@ hwkv_status hwkv_decode_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t 
     return launch_decode_merge(*L, group, ma, stream);
 }
 
+hwkv_status hwkv_decode_step(const hwkv_layout* L, const hwkv_cache* c, int32_t layer_begin,
+                             int32_t n_layers, int32_t n_seqs, const int32_t* seq_slots,
+                             const int64_t* pos, const void* k_new, const void* v_new,
+                             int32_t n_q_heads, const void* q, float scale, void* ws,
+                             uint64_t ws_bytes, void* out, hwkv_dtype out_dtype,
+                             hipStream_t stream) {
+    clear_error();
+    int group = 0;
+    DecodeSplitArgs a;
+    uint64_t rec_bytes = 0, need = 0;
+    // pos plays the part of ctx_len (context = pos + 1) in the shared checks
+    HWKV_TRY(split_args(L, c, layer_begin, n_layers, n_seqs, seq_slots, pos, n_q_heads, q, scale,
+                        ws, ws_bytes, &group, &a));
+    HWKV_TRY(hwkv_workspace_bytes(L, layer_begin, n_layers, n_seqs, n_q_heads, &rec_bytes));
+    HWKV_TRY(hwkv_step_workspace_bytes(L, layer_begin, n_layers, n_seqs, n_q_heads, &need));
+    if (ws_bytes < need)
+        return fail(HWKV_ERR_CAPACITY, "step workspace of " + std::to_string(ws_bytes) +
+                                           " bytes, need " + std::to_string(need));
+    if (!k_new || !v_new || !out) return fail(HWKV_ERR_INVALID_ARG, "null k_new, v_new or out");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16))
+        return fail(HWKV_ERR_MISALIGNED, "k_new, v_new and out must be 16-byte aligned");
+    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16)
+        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32 or HWKV_BF16");
+    a.k_new = static_cast<const uint8_t*>(k_new);
+    a.v_new = static_cast<const uint8_t*>(v_new);
+    a.pool_w = static_cast<uint8_t*>(c->pool);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + (rec_bytes + 255) / 256 * 256);
+    a.out = out;
+    a.out_bf16 = out_dtype == HWKV_BF16 ? 1 : 0;
+    a.n_kv_heads = L->n_kv_heads;
+    a.n_layers = n_layers;
+    return launch_decode_step(*L, group, a, stream);
+}
+
 hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
                               int32_t n_seqs, const int32_t* seq_slots, const int64_t* pos0,
                               int32_t n_chunk, int32_t n_q_heads, const void* q, const void* k,

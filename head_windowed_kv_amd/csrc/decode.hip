@@ -235,7 +235,123 @@ __device__ __forceinline__ void process_block(BlockRegs<BF16, D, G>& br, const b
     }
 }
 
-template <bool BF16, int D, int G>
+// Split records that another workgroup of the same launch reads (fused
+// step): stored and loaded as relaxed agent-scope atomics, i.e. accesses
+// that are coherent across the XCDs' separate L2 caches by themselves, so
+// no whole-cache write-back or invalidate is needed to hand them over.
+__device__ __forceinline__ void rec_put(float* p, float v, bool coherent) {
+    if (coherent)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+__device__ __forceinline__ float rec_get(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Output row of (layer, sequence, kv head): G query heads x D, fp32 or bf16.
+__device__ __forceinline__ void store_out4(void* out, bool bf16, int64_t at, f32x4 o) {
+    if (bf16) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(o.x) | ((uint32_t)f32_to_bf16_rne(o.y) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(o.z) | ((uint32_t)f32_to_bf16_rne(o.w) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + at) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + at) = o;
+    }
+}
+
+// Merge geometry: one thread per float4 of a record's acc[G][D] (NE4 of
+// them) times SG split groups; split s is folded by group s % SG, and the SG
+// partial sums are added in a fixed order.  Many splits are read in parallel
+// instead of one after another.
+template <int D, int G>
+struct MergeCfg {
+    static constexpr int NE4 = G * D / 4;
+    static constexpr int SG = (1024 / NE4) < 16 ? (1024 / NE4) : 16;
+    static constexpr int THREADS = NE4 * SG;
+    static constexpr int WAVES = (THREADS + 63) / 64;
+};
+
+// The merge of one (layer, sequence, kv head) done by the 256 threads of the
+// split workgroup that finished last: the same operations, in the same order,
+// as decode_merge_kernel, so both paths give identical bits.
+template <int D, int G>
+__device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, void* out, bool bf16,
+                                   int64_t obase) {
+    typedef MergeCfg<D, G> M;
+    constexpr int kPairs = M::NE4 * M::SG;
+    __shared__ float s_red[kWaves][G];
+    __shared__ float s_max[G];
+    __shared__ f32x4 s_num[M::SG][M::NE4];
+    __shared__ float s_den[M::SG][G];
+    const int t = threadIdx.x;
+    float mloc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) mloc[hh] = -INFINITY;
+    for (int s = t; s < ns; s += kThreads) {
+#pragma unroll
+        for (int hh = 0; hh < G; hh++)
+            mloc[hh] = fmaxf(mloc[hh], rec_get(rec0 + (int64_t)s * rec_floats + G * D + hh));
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) {
+        float x = mloc[hh];
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 8, 64));
+        x = fmaxf(x, __shfl_xor(x, 4, 64));
+        x = fmaxf(x, __shfl_xor(x, 2, 64));
+        x = fmaxf(x, __shfl_xor(x, 1, 64));
+        if ((t & 63) == 0) s_red[t >> 6][hh] = x;
+    }
+    __syncthreads();
+    if (t < G) {
+        float x = s_red[0][t];
+        for (int w = 1; w < kWaves; w++) x = fmaxf(x, s_red[w][t]);
+        s_max[t] = x;
+    }
+    __syncthreads();
+    for (int pr = t; pr < kPairs; pr += kThreads) {
+        const int e4 = pr % M::NE4, sg = pr / M::NE4;
+        const int h = (e4 * 4) / D;
+        const float Mh = s_max[h];
+        const bool den_thread = (e4 * 4) % D == 0;
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+#pragma unroll 4
+        for (int s = sg; s < ns; s += M::SG) {
+            const float* rs = rec0 + (int64_t)s * rec_floats;
+            const float f = fast_exp2(rec_get(rs + G * D + h) - Mh);
+            const f32x4 v = {rec_get(rs + e4 * 4), rec_get(rs + e4 * 4 + 1),
+                             rec_get(rs + e4 * 4 + 2), rec_get(rs + e4 * 4 + 3)};
+            num.x = fmaf(f, v.x, num.x);
+            num.y = fmaf(f, v.y, num.y);
+            num.z = fmaf(f, v.z, num.z);
+            num.w = fmaf(f, v.w, num.w);
+            if (den_thread) den = fmaf(f, rec_get(rs + G * D + G + h), den);
+        }
+        s_num[sg][e4] = num;
+        if (den_thread) s_den[sg][h] = den;
+    }
+    __syncthreads();
+    if (t < M::NE4) {
+        const int h = (t * 4) / D;
+        f32x4 tot = s_num[0][t];
+        float dtot = s_den[0][h];
+        for (int k = 1; k < M::SG; k++) {
+            const f32x4 x = s_num[k][t];
+            tot.x += x.x;
+            tot.y += x.y;
+            tot.z += x.z;
+            tot.w += x.w;
+            dtot += s_den[k][h];
+        }
+        store_out4(out, bf16, obase + t * 4,
+                   f32x4{tot.x / dtot, tot.y / dtot, tot.z / dtot, tot.w / dtot});
+    }
+}
+
+template <bool BF16, int D, int G, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs a) {
     typedef SplitCfg<BF16, D, G> C;
     typedef typename Elem<BF16>::Chunk Chunk;
@@ -250,11 +366,33 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     const int b = blockIdx.y;
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
+    if (fp != a.fingerprint) {
+        // meta of another layout: the split stage leaves no record (the
+        // merge stage reports NaN); the fused step writes NaN everywhere
+        if constexpr (FUSED) {
+            const int64_t n4 = (int64_t)a.n_layers * a.n_seqs * a.n_q_heads * (D / 4);
+            const int64_t stride = (int64_t)gridDim.x * gridDim.y * kThreads;
+            const float x = __builtin_nanf("");
+            for (int64_t e = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+                 e < n4; e += stride)
+                store_out4(a.out, a.out_bf16, e * 4, f32x4{x, x, x, x});
+        }
+        return;
+    }
     const WorkItem wk = a.work[a.work_begin + blockIdx.x];
-    if (fp != a.fingerprint) return;  // the merge stage reports this as NaN
     const HeadDesc hd = a.heads[wk.head_index];
-    const int64_t L = a.ctx_len[b];
-    if (L <= 0) return;
+    const int64_t L = FUSED ? a.ctx_len[b] + 1 : a.ctx_len[b];
+    const int rel_layer = hd.layer - a.layer_begin;
+    const int64_t obase =
+        (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
+    if (L <= 0) {
+        if constexpr (FUSED) {  // no context: zeros, as the merge stage writes
+            if (wk.split == 0)
+                for (int e = threadIdx.x; e < G * D / 4; e += kThreads)
+                    store_out4(a.out, a.out_bf16, obase + e * 4, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        return;
+    }
     // Window [lo, L).  Splits are cut on block boundaries: split j covers
     // the logical blocks [bA + j*SB, bA + (j+1)*SB) with bA = lo / 16 and
     // SB = split_tokens / 16, except that the last split runs to the
@@ -271,13 +409,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     const int64_t lb1 = wk.split == ns - 1 ? bZ : lb0 + SB - 1;
     float* rec = a.ws + ((int64_t)b * a.n_work_range + blockIdx.x) * a.rec_floats;
 
+    // Fused step: after this workgroup's record is written, count its arrival;
+    // the last of the head's ns splits merges all of them and re-arms the
+    // counter (nothing waits, so no workgroup can hang on another).  The
+    // record stores are agent-coherent; waiting for all of them to complete
+    // (vmcnt 0) before the workgroup barrier and the counter increment makes
+    // them visible to whichever workgroup draws the last ticket, which reads
+    // them with agent-coherent loads.
+    auto arrive_and_merge = [&]() {
+        if constexpr (FUSED) {
+            __shared__ uint32_t s_old;
+            uint32_t* cnt = a.counters + ((int64_t)rel_layer * a.n_kv_heads + hd.head) * a.n_seqs + b;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0)
+                s_old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (s_old != (uint32_t)(ns - 1)) return;
+            const float* rec0 =
+                a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
+            merge_in_workgroup<D, G>(rec0, (int)ns, a.rec_floats, a.out, a.out_bf16, obase);
+            if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
     const int64_t slot = a.seq_slots ? (int64_t)a.seq_slots[b] : (int64_t)b;
     if (slot < 0 || slot >= a.table_rows) {  // invalid slot: an empty record -> NaN output
-        for (int e = threadIdx.x; e < G * D; e += kThreads) rec[e] = 0.f;
+        for (int e = threadIdx.x; e < G * D; e += kThreads) rec_put(rec + e, 0.f, FUSED);
         if (threadIdx.x < G) {
-            rec[G * D + threadIdx.x] = -INFINITY;
-            rec[G * D + G + threadIdx.x] = 0.f;
+            rec_put(rec + G * D + threadIdx.x, -INFINITY, FUSED);
+            rec_put(rec + G * D + G + threadIdx.x, 0.f, FUSED);
         }
+        arrive_and_merge();
         return;
     }
     const int32_t* tbl = a.block_ids + slot * a.blocks_per_seq + hd.table_off;
@@ -295,10 +458,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         my_id = tbl[j];
     }
 
+    // Fused step: the new token (position L - 1, logical block bZ) belongs to
+    // the last split.  That workgroup writes its K/V rows into the ring slot
+    // (the slot's previous token lies outside every window that reads the
+    // block) and folds the rows from the arguments, not from the pool.
+    const bool new_here = FUSED && wk.split == ns - 1;
+    const int64_t kv_new_off =
+        (((int64_t)rel_layer * a.n_seqs + b) * a.n_kv_heads + hd.head) * (int64_t)C::ROW;
+    if constexpr (FUSED) {
+        if (new_here && wave == 0 && lane < 2 * (C::ROW / 16)) {
+            const int32_t id = tbl[(uint32_t)(bZ % nb)];
+            if (id >= 0 && (uint64_t)id < a.n_pool_blocks) {
+                const int half = lane / (C::ROW / 16), ch = lane % (C::ROW / 16);
+                const uint8_t* src = (half ? a.v_new : a.k_new) + kv_new_off + ch * 16;
+                uint8_t* dst = a.pool_w + (uint64_t)id * a.block_bytes +
+                               ((int64_t)half * kBS + (L - 1) % kBS) * C::ROW + ch * 16;
+                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+            }
+        }
+    }
+
     // query chunks of the G heads of this group
     Chunk qv[G][C::NC];
     {
-        const int rel_layer = hd.layer - a.layer_begin;
         const int64_t qoff =
             (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
         const uint8_t* qb = a.q + qoff * C::EB;
@@ -328,6 +510,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     auto fold = [&](BlockRegs<BF16, D, G>& br, int i, bool ok) {
         const int64_t lb = lb0 + wave + (int64_t)i * kWaves;
         const int64_t first = lb * kBS;
+        if constexpr (FUSED) {
+            if (new_here && lb == bZ) {  // the new token's row from the arguments
+                const int row = (int)((L - 1) % kBS);
+#pragma unroll
+                for (int rho = 0; rho < C::ROWS; rho++) {
+                    if (g + 8 * rho == row) {
+#pragma unroll
+                        for (int c = 0; c < C::NC; c++) {
+                            br.k[rho][c] = *reinterpret_cast<const Chunk*>(a.k_new + kv_new_off +
+                                                                           (c * 8 + r) * 16);
+                            br.v[rho][c] = *reinterpret_cast<const Chunk*>(a.v_new + kv_new_off +
+                                                                           (c * 8 + r) * 16);
+                        }
+                    }
+                }
+            }
+        }
         if (ok && first >= lo && first + kBS <= L) {
             process_block<BF16, D, G, true>(br, nullptr, qv, a.qk_scale_log2, m, l, acc);
         } else {
@@ -393,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         float sum = 0.f;
 #pragma unroll
         for (int sl = 0; sl < 2 * kWaves; sl++) sum += s_acc[sl][e];
-        rec[e] = sum;
+        rec_put(rec + e, sum, FUSED);
     }
     if (threadIdx.x < G) {
         const int h = threadIdx.x;
@@ -403,22 +602,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
 #pragma unroll
         for (int sl = 0; sl < 2 * kWaves; sl++) lsum += s_l[sl][h];
-        rec[G * D + h] = MW;
-        rec[G * D + G + h] = lsum;
+        rec_put(rec + G * D + h, MW, FUSED);
+        rec_put(rec + G * D + G + h, lsum, FUSED);
     }
+    arrive_and_merge();
 }
-
-// Merge geometry: one thread per float4 of a record's acc[G][D] (NE4 of
-// them) times SG split groups; split s is folded by group s % SG, and the SG
-// partial sums are added in a fixed order.  Many splits are read in parallel
-// instead of one after another.
-template <int D, int G>
-struct MergeCfg {
-    static constexpr int NE4 = G * D / 4;
-    static constexpr int SG = (1024 / NE4) < 16 ? (1024 / NE4) : 16;
-    static constexpr int THREADS = NE4 * SG;
-    static constexpr int WAVES = (THREADS + 63) / 64;
-};
 
 template <int D, int G>
 __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel(DecodeMergeArgs a) {
@@ -439,15 +627,7 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     const int64_t obase =
         (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)head * G) * D + e4 * 4;
 
-    auto store = [&](f32x4 o) {
-        if (a.out_bf16) {
-            const uint32_t lo = (uint32_t)f32_to_bf16_rne(o.x) | ((uint32_t)f32_to_bf16_rne(o.y) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16_rne(o.z) | ((uint32_t)f32_to_bf16_rne(o.w) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + obase) = make_uint2(lo, hi);
-        } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase) = o;
-        }
-    };
+    auto store = [&](f32x4 o) { store_out4(a.out, a.out_bf16, obase, o); };
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
     const int64_t L = a.ctx_len[b];
@@ -525,13 +705,14 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     }
 }
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool FUSED>
 hwkv_status launch_split_t(const DecodeSplitArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_work_range, (unsigned)a.n_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<BF16, D, G>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<BF16, D, G, FUSED>), grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
-        return fail(HWKV_ERR_HIP, std::string("decode split launch: ") + hipGetErrorString(e));
+        return fail(HWKV_ERR_HIP, std::string(FUSED ? "decode step launch: " : "decode split launch: ") +
+                                      hipGetErrorString(e));
     return HWKV_OK;
 }
 
@@ -559,23 +740,34 @@ bool decode_supported(hwkv_dtype dt, int head_dim, int group) {
     }
 }
 
-hwkv_status launch_decode_split(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
-                                hipStream_t s) {
+template <bool FUSED>
+hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
+                             hipStream_t s) {
     if (a.n_work_range <= 0) return HWKV_OK;
     const bool bf16 = lay.dtype == HWKV_BF16;
 #define HWKV_CASE(GG)                                                                      \
     case GG:                                                                               \
         if (bf16)                                                                          \
-            return lay.head_dim == 128 ? launch_split_t<true, 128, GG>(a, s)               \
-                                       : launch_split_t<true, 64, GG>(a, s);               \
-        return lay.head_dim == 128 ? launch_split_t<false, 128, GG>(a, s)                  \
-                                   : launch_split_t<false, 64, GG>(a, s);
+            return lay.head_dim == 128 ? launch_split_t<true, 128, GG, FUSED>(a, s)        \
+                                       : launch_split_t<true, 64, GG, FUSED>(a, s);        \
+        return lay.head_dim == 128 ? launch_split_t<false, 128, GG, FUSED>(a, s)           \
+                                   : launch_split_t<false, 64, GG, FUSED>(a, s);
     switch (group) {
         HWKV_FOR_GROUPS(HWKV_CASE)
         default: break;
     }
 #undef HWKV_CASE
     return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for GQA group " + std::to_string(group));
+}
+
+hwkv_status launch_decode_split(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
+                                hipStream_t s) {
+    return launch_split_any<false>(lay, group, a, s);
+}
+
+hwkv_status launch_decode_step(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
+                               hipStream_t s) {
+    return launch_split_any<true>(lay, group, a, s);
 }
 
 hwkv_status launch_decode_merge(const hwkv_layout& lay, int group, const DecodeMergeArgs& a,

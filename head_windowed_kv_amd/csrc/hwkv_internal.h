@@ -127,6 +127,18 @@ struct DecodeSplitArgs {
     int32_t split_tokens;
     int32_t rec_floats;
     float qk_scale_log2;  // scale * log2(e)
+    // Fused decode step only (hwkv_decode_step): ctx_len then holds the new
+    // token's position (context = position + 1); the token's K/V rows are
+    // appended by the split that covers it, and the last split of a head to
+    // finish (per-(layer, kv head, sequence) arrival counter) merges.
+    const uint8_t* k_new;
+    const uint8_t* v_new;
+    uint8_t* pool_w;
+    uint32_t* counters;
+    void* out;
+    int32_t out_bf16;
+    int32_t n_kv_heads;
+    int32_t n_layers;
 };
 
 struct DecodeMergeArgs {
@@ -172,6 +184,8 @@ hwkv_status launch_decode_merge(const hwkv_layout& lay, int group, const DecodeM
                                 hipStream_t s);
 hwkv_status launch_prefill(const hwkv_layout& lay, int group, const PrefillArgs& a,
                            hipStream_t s);
+hwkv_status launch_decode_step(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
+                               hipStream_t s);
 
 // Whether a kernel instance exists for (dtype, head_dim, group).
 bool decode_supported(hwkv_dtype dt, int head_dim, int group);

@@ -280,4 +280,15 @@ hwkv_status hwkv_workspace_bytes(const hwkv_layout* L, int32_t layer_begin, int3
     return HWKV_OK;
 }
 
+hwkv_status hwkv_step_workspace_bytes(const hwkv_layout* L, int32_t layer_begin, int32_t n_layers,
+                                      int32_t n_seqs, int32_t n_q_heads, uint64_t* bytes) {
+    uint64_t rec = 0;
+    hwkv_status st = hwkv_workspace_bytes(L, layer_begin, n_layers, n_seqs, n_q_heads, &rec);
+    if (st != HWKV_OK) return st;
+    // records, then one uint32 arrival counter per (layer, kv head, sequence)
+    const uint64_t counters = (uint64_t)n_layers * (uint64_t)L->n_kv_heads * (uint64_t)n_seqs * 4u;
+    *bytes = (rec + 255) / 256 * 256 + counters;
+    return HWKV_OK;
+}
+
 }  // extern "C"

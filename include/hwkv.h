@@ -217,6 +217,32 @@ hwkv_status hwkv_decode_attn(const hwkv_layout *layout, const hwkv_cache *cache,
                              void *workspace, uint64_t workspace_bytes, void *out,
                              hwkv_dtype out_dtype, hipStream_t stream);
 
+/* Device workspace of hwkv_decode_step: the hwkv_workspace_bytes records,
+ * padded to 256 bytes, then one uint32 arrival counter per (layer, kv head,
+ * sequence).  The counters must be zero before the first hwkv_decode_step on
+ * a workspace (zero-fill it once); every call leaves them zero again. */
+hwkv_status hwkv_step_workspace_bytes(const hwkv_layout *layout, int32_t layer_begin,
+                                      int32_t n_layers, int32_t n_seqs,
+                                      int32_t n_q_heads, uint64_t *bytes);
+
+/* One decode step in a single launch: the effect of hwkv_append of one token
+ * at position pos[b] (k_new, v_new: device [n_layers][n_seqs][n_kv_heads]
+ * [head_dim]) followed by hwkv_decode_attn with ctx_len = pos + 1, with the
+ * same results bit for bit.  The split that covers the new token also writes
+ * it into its ring slot (that slot's previous token is outside every window
+ * that reads the block, page 2 "SWA Window") and takes its K/V rows from the
+ * arguments; each split counts its arrival in the workspace and the last one
+ * of a head merges, so no separate merge launch is needed.  Two calls that
+ * overlap on one workspace race (they share the counters).  A sequence with
+ * pos < 0 gets zeros and no append; an invalid slot gets NaN and no append. */
+hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
+                             int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                             const int32_t *seq_slots, const int64_t *pos,
+                             const void *k_new, const void *v_new, int32_t n_q_heads,
+                             const void *q, float scale, void *workspace,
+                             uint64_t workspace_bytes, void *out, hwkv_dtype out_dtype,
+                             hipStream_t stream);
+
 /* Chunked prefill of one layer: sequence b has history [0, P) in the cache,
  * P = pos0[b], and n_chunk new tokens at [P, P+n_chunk).  Query row r
  * (position p = P + r) of query head i attends to kv head i / G over
