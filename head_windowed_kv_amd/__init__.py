@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 HWKV_F32 = 0
 HWKV_BF16 = 1
+HWKV_F16 = 2
 ABI_VERSION = 1
 
 STATUS_NAMES = {0: "HWKV_OK", 1: "HWKV_ERR_INVALID_ARG", 2: "HWKV_ERR_UNSUPPORTED",
@@ -36,7 +37,8 @@ STATUS_NAMES = {0: "HWKV_OK", 1: "HWKV_ERR_INVALID_ARG", 2: "HWKV_ERR_UNSUPPORTE
 
 #: every symbol the C ABI exports
 EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_layout_destroy",
-            "hwkv_layout_query", "hwkv_mem_estimate", "hwkv_table_fill", "hwkv_meta_fill",
+            "hwkv_layout_query", "hwkv_mem_estimate", "hwkv_capacity_check", "hwkv_table_fill",
+            "hwkv_meta_fill",
             "hwkv_workspace_bytes", "hwkv_append", "hwkv_decode_split", "hwkv_decode_merge",
             "hwkv_decode_attn", "hwkv_step_workspace_bytes", "hwkv_decode_step",
             "hwkv_prefill_attn")
@@ -74,6 +76,8 @@ _lib.hwkv_layout_query.restype = ctypes.c_int
 _lib.hwkv_layout_query.argtypes = [_vp, _P(hwkv_layout_desc), _vp, _vp, _vp]
 _lib.hwkv_mem_estimate.restype = ctypes.c_int
 _lib.hwkv_mem_estimate.argtypes = [_vp, _i64, _P(_u64)]
+_lib.hwkv_capacity_check.restype = ctypes.c_int
+_lib.hwkv_capacity_check.argtypes = [_vp, _i64, _u64, _P(_i64), _P(_i32), _P(_i32)]
 _lib.hwkv_table_fill.restype = ctypes.c_int
 _lib.hwkv_table_fill.argtypes = [_vp, _i64, _vp]
 _lib.hwkv_meta_fill.restype = ctypes.c_int
@@ -127,11 +131,14 @@ def _dtype_code(dtype) -> int:
         return HWKV_BF16
     if dtype in (torch.float32, "f32", HWKV_F32):
         return HWKV_F32
-    raise ValueError("dtype must be torch.bfloat16 or torch.float32, got %r" % (dtype,))
+    if dtype in (torch.float16, "f16", HWKV_F16):
+        return HWKV_F16
+    raise ValueError("dtype must be torch.bfloat16, torch.float16 or torch.float32, got %r"
+                     % (dtype,))
 
 
 def torch_dtype(code: int) -> torch.dtype:
-    return torch.bfloat16 if code == HWKV_BF16 else torch.float32
+    return {HWKV_BF16: torch.bfloat16, HWKV_F16: torch.float16}.get(code, torch.float32)
 
 
 class Layout:
@@ -188,6 +195,19 @@ def hwkv_mem_estimate(layout: Layout, n_seqs: int) -> int:
     b = ctypes.c_uint64()
     _check(_lib.hwkv_mem_estimate(layout.handle, n_seqs, ctypes.byref(b)))
     return int(b.value)
+
+
+def hwkv_capacity_check(layout: Layout, n_seqs: int, pool_bytes: int):
+    """None if the pool holds n_seqs rows, else (seq_row, layer, head, message)
+    of the first head whose blocks do not fit."""
+    row, layer, head = ctypes.c_int64(-1), ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = _lib.hwkv_capacity_check(layout.handle, n_seqs, pool_bytes, ctypes.byref(row),
+                                  ctypes.byref(layer), ctypes.byref(head))
+    if st == 0:
+        return None
+    if STATUS_NAMES.get(st) != "HWKV_ERR_CAPACITY":
+        _check(st)
+    return int(row.value), int(layer.value), int(head.value), hwkv_last_error()
 
 
 def hwkv_table_fill(layout: Layout, n_seqs: int) -> np.ndarray:

@@ -28,26 +28,7 @@ hwkv_status check_cache(const hwkv_layout* L, const hwkv_cache* c) {
     if (!aligned(c->pool, 256) || !aligned(c->block_ids, 256) || !aligned(c->meta, 256))
         return fail(HWKV_ERR_MISALIGNED, "pool, block_ids and meta must be 256-byte aligned");
     if (c->table_rows < 1) return fail(HWKV_ERR_INVALID_ARG, "table_rows must be >= 1");
-    uint64_t need = 0;
-    hwkv_status st = hwkv_mem_estimate(L, c->table_rows, &need);
-    if (st != HWKV_OK) return st;
-    if (c->pool_bytes < need) {
-        const uint64_t avail = c->pool_bytes / L->block_bytes;
-        const uint64_t bps = (uint64_t)L->blocks_per_seq;
-        const uint64_t row = avail / bps;
-        const uint64_t left = avail - row * bps;
-        size_t i = 0;
-        while (i + 1 < L->nblocks.size() &&
-               (uint64_t)(L->head_off[i] + L->nblocks[i]) <= left)
-            i++;
-        return fail(HWKV_ERR_CAPACITY,
-                    "KV cache block allocation failed at layer " +
-                        std::to_string(i / L->n_kv_heads) + ", head " +
-                        std::to_string(i % L->n_kv_heads) + ": sequence row " +
-                        std::to_string(row) + " needs " + std::to_string(need) +
-                        " pool bytes in total, the pool has " + std::to_string(c->pool_bytes));
-    }
-    return HWKV_OK;
+    return hwkv_capacity_check(L, c->table_rows, c->pool_bytes, nullptr, nullptr, nullptr);
 }
 
 hwkv_status check_batch(const hwkv_layout* L, const hwkv_cache* c, int32_t layer_begin,
@@ -108,6 +89,10 @@ hwkv_status hwkv_append(const hwkv_layout* L, const hwkv_cache* c, int32_t layer
     clear_error();
     HWKV_TRY(check_cache(L, c));
     HWKV_TRY(check_batch(L, c, layer_begin, n_layers, n_seqs, seq_slots));
+    if (!append_supported(*L))
+        return fail(HWKV_ERR_UNSUPPORTED, "no append kernel for rows of " +
+                                              std::to_string(L->head_dim * elem_bytes(L->dtype)) +
+                                              " bytes (rows must be a multiple of 16 bytes)");
     if (n_new < 1) return fail(HWKV_ERR_INVALID_ARG, "n_new must be >= 1");
     if (!pos0 || !k || !v) return fail(HWKV_ERR_INVALID_ARG, "null pos0, k or v");
     if (!aligned(pos0, 8)) return fail(HWKV_ERR_MISALIGNED, "pos0 must be 8-byte aligned");
@@ -135,6 +120,8 @@ hwkv_status hwkv_append(const hwkv_layout* L, const hwkv_cache* c, int32_t layer
     a.n_seqs = n_seqs;
     a.n_new = n_new;
     a.n_kv_heads = L->n_kv_heads;
+    a.block_size = L->block_size;
+    a.row_chunks = (int32_t)(row_bytes / 16);
     a.n_chunks = (int64_t)(rows * row_bytes / 16);
     return launch_append(*L, a, stream);
 }
@@ -147,9 +134,9 @@ static hwkv_status split_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     HWKV_TRY(check_cache(L, c));
     HWKV_TRY(check_batch(L, c, layer_begin, n_layers, n_seqs, seq_slots));
     HWKV_TRY(check_group(L, n_q_heads, group));
-    if (!decode_supported(L->dtype, L->head_dim, *group))
-        return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for this dtype, head_dim and GQA "
-                                          "group size " + std::to_string(*group));
+    if (!decode_supported(*L, *group))
+        return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for this block size, dtype, head_dim "
+                                          "and GQA group size " + std::to_string(*group));
     HWKV_TRY(check_workspace(L, layer_begin, n_layers, n_seqs, n_q_heads, ws, ws_bytes));
     if (!ctx_len || !q) return fail(HWKV_ERR_INVALID_ARG, "null ctx_len or q");
     if (!aligned(ctx_len, 8)) return fail(HWKV_ERR_MISALIGNED, "ctx_len must be 8-byte aligned");
@@ -188,9 +175,9 @@ static hwkv_status merge_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     HWKV_TRY(check_cache(L, c));
     HWKV_TRY(check_batch(L, c, layer_begin, n_layers, n_seqs, nullptr));
     HWKV_TRY(check_group(L, n_q_heads, group));
-    if (!decode_supported(L->dtype, L->head_dim, *group))
-        return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for this dtype, head_dim and GQA "
-                                          "group size " + std::to_string(*group));
+    if (!decode_supported(*L, *group))
+        return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for this block size, dtype, head_dim "
+                                          "and GQA group size " + std::to_string(*group));
     HWKV_TRY(check_workspace(L, layer_begin, n_layers, n_seqs, n_q_heads, ws, ws_bytes));
     if (!ctx_len || !out) return fail(HWKV_ERR_INVALID_ARG, "null ctx_len or out");
     if (!aligned(ctx_len, 8)) return fail(HWKV_ERR_MISALIGNED, "ctx_len must be 8-byte aligned");
@@ -303,9 +290,9 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t
     HWKV_TRY(check_batch(L, c, layer, 1, n_seqs, seq_slots));
     int group = 0;
     HWKV_TRY(check_group(L, n_q_heads, &group));
-    if (!prefill_supported(L->dtype, L->head_dim, group))
-        return fail(HWKV_ERR_UNSUPPORTED, "no prefill kernel for this dtype, head_dim and GQA "
-                                          "group size " + std::to_string(group));
+    if (!prefill_supported(*L, group))
+        return fail(HWKV_ERR_UNSUPPORTED, "no prefill kernel for this block size, dtype, "
+                                          "head_dim and GQA group size " + std::to_string(group));
     if (n_chunk < 1) return fail(HWKV_ERR_INVALID_ARG, "n_chunk must be >= 1");
     if (!pos0 || !q || !k || !v || !out)
         return fail(HWKV_ERR_INVALID_ARG, "null pos0, q, k, v or out");

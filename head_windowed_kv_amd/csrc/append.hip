@@ -3,8 +3,9 @@
 // HeadWiseKV write-up, 核心技术 2: every head owns ceil(w_h / block_size)
 // blocks.  Page 2 ("KV Cache Consistency Practices ..."), "SWA Window": only
 // the most recent tokens are kept and the window moves with the sequence.
-// Token t of a head with nb blocks is stored in ring block (t / 16) % nb, row
-// t % 16, so the ring always holds the newest C = 16 * nb >= w_h tokens.
+// Token t of a head with nb blocks of bs tokens is stored in ring block
+// (t / bs) % nb, row t % bs, so the ring always holds the newest
+// C = bs * nb >= w_h tokens.
 //
 // One thread moves one 16-byte chunk of a K row and the same chunk of the V
 // row.  Threads are numbered in the input's memory order
@@ -20,12 +21,12 @@
 namespace hwkv {
 namespace {
 
-constexpr int kBS = 16;
 constexpr int kThreads = 256;
 
-template <int ROW>  // bytes per K (or V) row
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
-    constexpr int CPR = ROW / 16;  // 16-byte chunks per row
+    const int CPR = a.row_chunks;  // 16-byte chunks per row
+    const int64_t ROW = (int64_t)CPR * 16;
+    const int64_t bs = a.block_size;
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
     if (fp != a.fingerprint) return;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -43,45 +44,37 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         if (P < 0) continue;
         const HeadDesc hd = a.heads[(int64_t)(a.layer_begin + li) * a.n_kv_heads + h];
         const int64_t t = P + tok;
-        const int64_t cap = (int64_t)hd.nblocks * kBS;
+        const int64_t cap = (int64_t)hd.nblocks * bs;
         if (t < P + a.n_new - cap) continue;  // overwritten later in this call
         const int64_t slot = a.seq_slots ? (int64_t)a.seq_slots[b] : (int64_t)b;
         if (slot < 0 || slot >= a.table_rows) continue;
         const int32_t id =
-            a.block_ids[slot * a.blocks_per_seq + hd.table_off + (t / kBS) % hd.nblocks];
+            a.block_ids[slot * a.blocks_per_seq + hd.table_off + (t / bs) % hd.nblocks];
         if (id < 0 || (uint64_t)id >= a.n_pool_blocks) continue;
-        uint8_t* dst = a.pool + (uint64_t)id * a.block_bytes + (uint64_t)(t % kBS) * ROW + c * 16;
+        uint8_t* dst = a.pool + (uint64_t)id * a.block_bytes + (uint64_t)(t % bs) * ROW + c * 16;
         const uint4 kc = *reinterpret_cast<const uint4*>(a.k + idx * 16);
         const uint4 vc = *reinterpret_cast<const uint4*>(a.v + idx * 16);
         *reinterpret_cast<uint4*>(dst) = kc;
-        *reinterpret_cast<uint4*>(dst + kBS * ROW) = vc;
+        *reinterpret_cast<uint4*>(dst + bs * ROW) = vc;
     }
-}
-
-template <int ROW>
-hwkv_status launch_t(const AppendArgs& a, hipStream_t s) {
-    int64_t blocks = (a.n_chunks + kThreads - 1) / kThreads;
-    if (blocks > 16384) blocks = 16384;
-    if (blocks < 1) return HWKV_OK;
-    hipLaunchKernelGGL((append_kernel<ROW>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return fail(HWKV_ERR_HIP, std::string("append launch: ") + hipGetErrorString(e));
-    return HWKV_OK;
 }
 
 }  // namespace
 
+bool append_supported(const hwkv_layout& lay) {
+    // a bit copy in 16-byte chunks: any block size, rows of whole chunks
+    return ((int64_t)lay.head_dim * elem_bytes(lay.dtype)) % 16 == 0;
+}
+
 hwkv_status launch_append(const hwkv_layout& lay, const AppendArgs& a, hipStream_t s) {
-    const int row = lay.head_dim * elem_bytes(lay.dtype);
-    switch (row) {
-        case 128: return launch_t<128>(a, s);
-        case 256: return launch_t<256>(a, s);
-        case 512: return launch_t<512>(a, s);
-        default: break;
-    }
-    return fail(HWKV_ERR_UNSUPPORTED, "no append kernel for rows of " + std::to_string(row) +
-                                          " bytes");
+    int64_t blocks = (a.n_chunks + kThreads - 1) / kThreads;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) return HWKV_OK;
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(HWKV_ERR_HIP, std::string("append launch: ") + hipGetErrorString(e));
+    return HWKV_OK;
 }
 
 }  // namespace hwkv

@@ -731,9 +731,10 @@ hwkv_status launch_merge_t(const DecodeMergeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool decode_supported(hwkv_dtype dt, int head_dim, int group) {
-    if (dt != HWKV_F32 && dt != HWKV_BF16) return false;
-    if (head_dim != 64 && head_dim != 128) return false;
+bool decode_supported(const hwkv_layout& lay, int group) {
+    if (lay.block_size != kBS) return false;
+    if (lay.dtype != HWKV_F32 && lay.dtype != HWKV_BF16) return false;
+    if (lay.head_dim != 64 && lay.head_dim != 128) return false;
     switch (group) {
         case 1: case 2: case 3: case 4: case 6: case 8: return true;
         default: return false;

@@ -13,6 +13,16 @@ namespace hwkv {
 
 constexpr uint32_t kMetaMagic = 0x564B5748u;  // "HWKV"
 constexpr int kDefaultSplitTokens = 1024;
+constexpr int kMaxSplitTokens = 2048;
+constexpr int kMaxBlockSize = 1024;
+constexpr int kMaxHeadDim = 1024;
+
+// Default decode split length: the largest multiple of the block size not
+// above 1024 tokens (at least one block).
+inline int32_t default_split_tokens(int32_t block_size) {
+    const int32_t n = kDefaultSplitTokens / block_size;
+    return (n < 1 ? 1 : n) * block_size;
+}
 constexpr int kMetaAlign = 256;
 
 // Per-head descriptor in the device meta blob (32 bytes, one scalar load).
@@ -104,7 +114,9 @@ struct AppendArgs {
     const uint8_t* k;
     const uint8_t* v;
     int32_t layer_begin, n_layers, n_seqs, n_new, n_kv_heads;
-    int64_t n_chunks;  // total 16-byte chunks of K (same for V)
+    int32_t block_size;
+    int32_t row_chunks;  // 16-byte chunks per K (or V) row
+    int64_t n_chunks;    // total 16-byte chunks of K (same for V)
 };
 
 struct DecodeSplitArgs {
@@ -187,8 +199,10 @@ hwkv_status launch_prefill(const hwkv_layout& lay, int group, const PrefillArgs&
 hwkv_status launch_decode_step(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                                hipStream_t s);
 
-// Whether a kernel instance exists for (dtype, head_dim, group).
-bool decode_supported(hwkv_dtype dt, int head_dim, int group);
-bool prefill_supported(hwkv_dtype dt, int head_dim, int group);
+// Whether a kernel instance exists for a layout (block size, head_dim, dtype)
+// and GQA group size.
+bool append_supported(const hwkv_layout& lay);
+bool decode_supported(const hwkv_layout& lay, int group);
+bool prefill_supported(const hwkv_layout& lay, int group);
 
 }  // namespace hwkv

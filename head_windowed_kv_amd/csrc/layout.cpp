@@ -64,20 +64,22 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
         return fail(HWKV_ERR_INVALID_ARG, "n_layers and n_kv_heads must be >= 1");
     if ((int64_t)n_layers * n_kv_heads > (1 << 24))
         return fail(HWKV_ERR_INVALID_ARG, "more than 2^24 heads");
-    if (block_size < 1 || head_dim < 1)
-        return fail(HWKV_ERR_INVALID_ARG, "block_size and head_dim must be >= 1");
-    if (dtype != HWKV_F32 && dtype != HWKV_BF16)
-        return fail(HWKV_ERR_INVALID_ARG, "dtype must be HWKV_F32 or HWKV_BF16");
-    if (block_size != 16)
-        return fail(HWKV_ERR_UNSUPPORTED, "block_size " + std::to_string(block_size) +
-                                              " has no kernel (supported: 16)");
-    if (head_dim != 64 && head_dim != 128)
-        return fail(HWKV_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) +
-                                              " has no kernel (supported: 64, 128)");
-    if (split_tokens == 0) split_tokens = kDefaultSplitTokens;
-    if (split_tokens < block_size || split_tokens % block_size != 0 || split_tokens > 2048)
-        return fail(HWKV_ERR_INVALID_ARG,
-                    "split_tokens must be a multiple of block_size in [block_size, 2048]");
+    if (block_size < 1 || block_size > kMaxBlockSize || head_dim < 1 || head_dim > kMaxHeadDim)
+        return fail(HWKV_ERR_INVALID_ARG, "block_size must be in [1, " +
+                                              std::to_string(kMaxBlockSize) +
+                                              "] and head_dim in [1, " +
+                                              std::to_string(kMaxHeadDim) + "]");
+    if (dtype != HWKV_F32 && dtype != HWKV_BF16 && dtype != HWKV_F16)
+        return fail(HWKV_ERR_INVALID_ARG, "dtype must be HWKV_F32, HWKV_BF16 or HWKV_F16");
+    // A layout is a host description (block tables, the exact estimate); any
+    // block size and head_dim can be described.  Whether a kernel exists for
+    // it is checked by the device calls (HWKV_ERR_UNSUPPORTED there).
+    if (split_tokens == 0) split_tokens = default_split_tokens(block_size);
+    const int32_t max_split = block_size > kMaxSplitTokens ? block_size : kMaxSplitTokens;
+    if (split_tokens < block_size || split_tokens % block_size != 0 || split_tokens > max_split)
+        return fail(HWKV_ERR_INVALID_ARG, "split_tokens must be a multiple of block_size in "
+                                          "[block_size, max(block_size, " +
+                                              std::to_string(kMaxSplitTokens) + ")]");
 
     const int64_t n_heads = (int64_t)n_layers * n_kv_heads;
     for (int64_t i = 0; i < n_heads; i++) {
@@ -212,6 +214,34 @@ hwkv_status hwkv_mem_estimate(const hwkv_layout* L, int64_t n_seqs, uint64_t* by
         return fail(HWKV_ERR_OVERFLOW, "pool bytes overflow 64 bits");
     *bytes = per_seq * (uint64_t)n_seqs;
     return HWKV_OK;
+}
+
+hwkv_status hwkv_capacity_check(const hwkv_layout* L, int64_t n_seqs, uint64_t pool_bytes,
+                                int64_t* seq_row, int32_t* layer, int32_t* head) {
+    clear_error();
+    if (!L) return fail(HWKV_ERR_INVALID_ARG, "null layout");
+    if (n_seqs < 0) return fail(HWKV_ERR_INVALID_ARG, "n_seqs must be >= 0");
+    uint64_t need = 0;
+    hwkv_status st = hwkv_mem_estimate(L, n_seqs, &need);
+    if (st != HWKV_OK) return st;
+    if (pool_bytes >= need) return HWKV_OK;
+    // Blocks are laid out sequence row by row, heads layer-major inside a
+    // row: find the first head whose blocks end beyond the pool.
+    const uint64_t avail = pool_bytes / L->block_bytes;
+    const uint64_t bps = (uint64_t)L->blocks_per_seq;
+    const uint64_t row = avail / bps;
+    const uint64_t left = avail - row * bps;
+    size_t i = 0;
+    while (i + 1 < L->nblocks.size() && (uint64_t)(L->head_off[i] + L->nblocks[i]) <= left) i++;
+    const int32_t ly = (int32_t)(i / L->n_kv_heads), hh = (int32_t)(i % L->n_kv_heads);
+    if (seq_row) *seq_row = (int64_t)row;
+    if (layer) *layer = ly;
+    if (head) *head = hh;
+    return fail(HWKV_ERR_CAPACITY,
+                "KV cache block allocation failed at layer " + std::to_string(ly) + ", head " +
+                    std::to_string(hh) + ": sequence row " + std::to_string(row) + " needs " +
+                    std::to_string(need) + " pool bytes in total, the pool has " +
+                    std::to_string(pool_bytes));
 }
 
 hwkv_status hwkv_table_fill(const hwkv_layout* L, int64_t n_seqs, int32_t* block_ids) {

@@ -457,8 +457,9 @@ hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool prefill_supported(hwkv_dtype dt, int head_dim, int group) {
-    if (dt != HWKV_BF16 || (head_dim != 64 && head_dim != 128)) return false;
+bool prefill_supported(const hwkv_layout& lay, int group) {
+    if (lay.block_size != kBS) return false;
+    if (lay.dtype != HWKV_BF16 || (lay.head_dim != 64 && lay.head_dim != 128)) return false;
     switch (group) {
         case 1: case 2: case 3: case 4: case 6: case 8: return true;
         default: return false;

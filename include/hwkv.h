@@ -71,7 +71,8 @@ typedef enum hwkv_status {
 
 typedef enum hwkv_dtype {
     HWKV_F32 = 0,
-    HWKV_BF16 = 1
+    HWKV_BF16 = 1,
+    HWKV_F16 = 2
 } hwkv_dtype;
 
 typedef struct hwkv_layout hwkv_layout; /* opaque, host-side, immutable */
@@ -115,10 +116,16 @@ const char *hwkv_last_error(void);
 /* Build a layout from windows[n_layers*n_kv_heads] (layer-major, tokens per
  * head, each >= 1) -- the per-layer kv_head_windows vectors of the write-up's
  * policy YAML (核心技术 2).  Each head gets nblocks = ceil(w / block_size)
- * blocks.  Supported: block_size 16; head_dim 64 or 128; dtype F32 or BF16.
- * split_tokens is the decode split length S (a multiple of block_size, at
- * most 2048; 0 picks 1024).  On success *out owns the layout; free it with
- * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1), UNSUPPORTED, OVERFLOW. */
+ * blocks.  A layout is a host description: any block_size in [1, 1024],
+ * head_dim in [1, 1024] and dtype F32, BF16 or F16 can be described and
+ * estimated; the device calls report HWKV_ERR_UNSUPPORTED for combinations
+ * that have no kernel (kernels: block_size 16; head_dim 64 or 128; decode F32
+ * or BF16, prefill BF16; append any block size with rows of whole 16-byte
+ * chunks).  split_tokens is the decode split length S (a multiple of
+ * block_size, at most max(block_size, 2048); 0 picks the largest multiple of
+ * block_size not above 1024).  On success *out owns the layout; free it with
+ * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1, a size
+ * out of range), OVERFLOW. */
 hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads,
                                const int32_t *windows, int32_t block_size,
                                int32_t head_dim, hwkv_dtype dtype,
@@ -139,6 +146,17 @@ hwkv_status hwkv_layout_query(const hwkv_layout *layout, hwkv_layout_desc *desc,
  * Covers K and V blocks only (not tables, meta or workspace). */
 hwkv_status hwkv_mem_estimate(const hwkv_layout *layout, int64_t n_seqs,
                               uint64_t *bytes);
+
+/* Whether a pool of pool_bytes holds n_seqs sequence rows of this layout.
+ * HWKV_OK if pool_bytes >= hwkv_mem_estimate(n_seqs).  Otherwise
+ * HWKV_ERR_CAPACITY: blocks are laid out row by row, heads layer-major inside
+ * a row, and *seq_row, *layer, *head (each may be null) receive the first
+ * head whose blocks do not fit; the message has the form of the write-up's
+ * operations table ("KV cache block allocation failed at layer X, head Y").
+ * Every device call runs this check on its cache view. */
+hwkv_status hwkv_capacity_check(const hwkv_layout *layout, int64_t n_seqs,
+                                uint64_t pool_bytes, int64_t *seq_row,
+                                int32_t *layer, int32_t *head);
 
 /* Default block tables into host memory block_ids[n_seqs*blocks_per_seq]:
  * row s gets the consecutive ids [s*blocks_per_seq, (s+1)*blocks_per_seq).

@@ -120,14 +120,97 @@ def test_fingerprint_tracks_every_parameter():
 @pytest.mark.parametrize("args,status", [
     (([[0, 4]], 16, 128, "bf16"), "HWKV_ERR_INVALID_ARG"),
     (([[-5]], 16, 128, "bf16"), "HWKV_ERR_INVALID_ARG"),
-    (([[16]], 32, 128, "bf16"), "HWKV_ERR_UNSUPPORTED"),
-    (([[16]], 16, 96, "bf16"), "HWKV_ERR_UNSUPPORTED"),
+    (([[16]], 0, 128, "bf16"), "HWKV_ERR_INVALID_ARG"),
+    (([[16]], 2048, 128, "bf16"), "HWKV_ERR_INVALID_ARG"),
+    (([[16]], 16, 0, "bf16"), "HWKV_ERR_INVALID_ARG"),
+    (([[16]], 16, 1025, "bf16"), "HWKV_ERR_INVALID_ARG"),
     (([[16]], 16, 128, "bf16", 24), "HWKV_ERR_INVALID_ARG"),
+    (([[16]], 32, 128, "bf16", 48), "HWKV_ERR_INVALID_ARG"),
+    (([[16]], 16, 128, "bf16", 4096), "HWKV_ERR_INVALID_ARG"),
 ])
 def test_layout_create_errors(args, status):
     with pytest.raises(hw.HwkvError) as e:
         hw.hwkv_layout_create(*args)
     assert e.value.status_name == status
+
+
+@pytest.mark.parametrize("bs,d,dt", [(32, 128, "bf16"), (64, 256, "f16"), (48, 96, "f32"),
+                                     (1, 8, "bf16"), (1024, 1024, "f32")])
+def test_any_block_size_head_dim_and_dtype_can_be_described(bs, d, dt):
+    """A layout is a host description: sizes without a kernel still get exact
+    block counts and estimates (equal to the oracle's)."""
+    w = np.array([[1, 47, 1000], [4096, 65, 3]], np.int32)
+    lay = hw.hwkv_layout_create(w, bs, d, dt)
+    desc, _, nb, off = hw.hwkv_layout_query(lay)
+    ref_nb, ref_off, ref_bps = oracle.layout(w, bs)
+    assert np.array_equal(nb.reshape(-1), ref_nb) and np.array_equal(off, ref_off)
+    eb = {"bf16": 2, "f16": 2, "f32": 4}[dt]
+    for n in (0, 1, 7):
+        assert hw.hwkv_mem_estimate(lay, n) == oracle.mem_estimate(w, bs, d, eb, n)
+    # default decode split: the largest multiple of the block size <= 1024
+    assert desc.split_tokens == max(1, 1024 // bs) * bs
+
+
+def _unsupported_calls(lay, group):
+    """Status of append / decode / prefill on a fake cache view.  Each call
+    also carries one invalid argument that is checked after the kernel check
+    (n_new = 0, scale = inf, n_chunk = 0), so every call fails validation and
+    nothing is ever launched: UNSUPPORTED if no kernel exists, else
+    INVALID_ARG."""
+    cv = _fake_cache(lay, hw.hwkv_mem_estimate(lay, 1), 1)
+    p = [ctypes.c_void_p(x << 20) for x in range(4, 13)]
+    n_q = lay.desc().n_kv_heads * group
+    ws_bytes = 1 << 30
+    st_app = hw._lib.hwkv_append(lay.handle, ctypes.byref(cv), 0, 1, 1, None, p[0], 0, p[1], p[2],
+                                 None)
+    st_dec = hw._lib.hwkv_decode_attn(lay.handle, ctypes.byref(cv), 0, 1, 1, None, p[0], n_q,
+                                      p[3], float("inf"), ctypes.c_void_p(256 << 20), ws_bytes,
+                                      p[4], 0, None)
+    st_pf = hw._lib.hwkv_prefill_attn(lay.handle, ctypes.byref(cv), 0, 1, None, p[0], 0, n_q,
+                                      p[3], p[1], p[2], p[4], 0, 0.1, None)
+    return [hw.STATUS_NAMES[x] for x in (st_app, st_dec, st_pf)]
+
+
+@pytest.mark.parametrize("bs,d,dt,want", [
+    (32, 128, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+    (16, 128, "f16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+    (16, 128, "f32", ["ok", "ok", "HWKV_ERR_UNSUPPORTED"]),
+    (16, 4, "bf16", ["HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+])
+def test_device_calls_without_a_kernel_are_rejected_before_launch(bs, d, dt, want):
+    lay = hw.hwkv_layout_create([[64, 16]], bs, d, dt)
+    got = _unsupported_calls(lay, 3)
+    for g, w in zip(got, want):
+        assert g == ("HWKV_ERR_INVALID_ARG" if w == "ok" else w)
+
+
+def test_capacity_check_matches_a_walk_over_rows_and_heads():
+    """The first head whose blocks do not fit, found by walking sequence rows
+    and heads in allocation order (brute force over the oracle's layout)."""
+    w = np.array([synth.YAML_LAYER0, synth.YAML_LAYER1, [16, 1, 33, 5000, 7, 64, 1024, 3]],
+                 np.int32)
+    lay = hw.hwkv_layout_create(w, 16, 128, "bf16")
+    bb = lay.desc().block_bytes
+    nb, off, bps = oracle.layout(w, 16)
+    rng = np.random.default_rng(5)
+    n_seqs = 3
+    for avail in list(rng.integers(0, n_seqs * bps, 40)) + [0, bps - 1, bps, n_seqs * bps - 1]:
+        pool = int(avail) * bb + int(rng.integers(0, bb))
+        got = hw.hwkv_capacity_check(lay, n_seqs, pool)
+        # brute force: blocks end at row*bps + off[i] + nb[i]
+        want = None
+        for row in range(n_seqs):
+            for i in range(len(nb)):
+                if row * bps + off[i] + nb[i] > avail:
+                    want = (row, i // 8, i % 8)
+                    break
+            if want:
+                break
+        assert (got[:3] if got else None) == want, avail
+        if got:
+            assert got[3].startswith("KV cache block allocation failed at layer %d, head %d"
+                                     % (want[1], want[2]))
+    assert hw.hwkv_capacity_check(lay, n_seqs, n_seqs * bps * bb) is None
 
 
 def test_table_fill_overflow_is_reported():

@@ -13,14 +13,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_script(windows, dtype, d, n_seqs, table_rows, script, seed, slots=None, perm=False,
-                layer_begin=0, n_layers=None):
+                layer_begin=0, n_layers=None, block_size=16):
     H = hw()
     dev = device()
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     windows = np.asarray(windows, np.int32)
     L_all, n_kv = windows.shape
     n_layers = L_all - layer_begin if n_layers is None else n_layers
-    lay = H.hwkv_layout_create(windows, 16, d, dtype)
+    lay = H.hwkv_layout_create(windows, block_size, d, dtype)
     bps = lay.desc().blocks_per_seq
     rng = np.random.default_rng(seed)
     ids = (rng.permutation(table_rows * bps) if perm else np.arange(table_rows * bps))
@@ -37,7 +37,7 @@ def _run_script(windows, dtype, d, n_seqs, table_rows, script, seed, slots=None,
         v = synth.randn((n_layers, n_seqs, n_new, n_kv, d), tdt, g)
         p = torch.tensor(pos0, dtype=torch.int64, device=dev)
         H.hwkv_append(cache, layer_begin, n_layers, p, k, v, seq_slots=slot_t)
-        oracle.append(ref, ids, windows, 16, d, layer_begin, pos0, synth.to_raw(k),
+        oracle.append(ref, ids, windows, block_size, d, layer_begin, pos0, synth.to_raw(k),
                       synth.to_raw(v), seq_slots=slots)
         torch.cuda.synchronize()
         got = cache.pool.cpu().numpy()
@@ -69,6 +69,16 @@ def test_f32_d128_many_sequences():
     windows = [[16, 31, 129]]
     script = [([int(x) for x in np.arange(9) * 7], 40), ([int(x) for x in np.arange(9) * 7 + 40], 1)]
     _run_script(windows, "f32", 128, 9, 9, script, seed=204, perm=True)
+
+
+@pytest.mark.parametrize("block_size", [32, 64, 48, 1])
+def test_other_block_sizes(block_size):
+    """The append is a bit copy for any block size: ring block (t / bs) % nb,
+    row t % bs."""
+    windows = [[1, 15, 64, 65, 100, 512], [33, 7, 1024, 200, 64, 2]]
+    script = [([0, 5], 1), ([1, 6], 40), ([41, 46], 129), ([170, 175], 1100), ([1270, 1275], 3)]
+    _run_script(windows, "bf16", 64, 2, 3, script, seed=206 + block_size, perm=True,
+                block_size=block_size)
 
 
 def test_invalid_device_values_are_skipped_not_faulted():
