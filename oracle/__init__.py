@@ -24,6 +24,7 @@ _LIB = os.path.join(_HERE, "libhwkv_oracle.so")
 
 ELEM_F32 = 0
 ELEM_BF16 = 1
+ELEM_F16 = 2
 
 
 def build(force: bool = True) -> str:
@@ -69,6 +70,8 @@ def _load():
         lib.hwkvref_prefill.restype = i32
         lib.hwkvref_prefill.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp,
                                         vp, vp, vp, vp, vp, i64, i32, vp, dbl, vp]
+        lib.hwkvref_widen.restype = None
+        lib.hwkvref_widen.argtypes = [vp, i64, i32, vp]
         lib.hwkvref_threads.restype = i32
         lib.hwkvref_threads.argtypes = []
         lib.hwkvref_set_threads.restype = None
@@ -90,12 +93,24 @@ def _i64(a) -> np.ndarray:
 
 
 def elem_code(raw: np.ndarray) -> int:
-    """fp32 arrays are float32; bf16 arrays are carried as their uint16 bits."""
+    """fp32 arrays are float32; bf16 arrays are carried as their uint16 bits;
+    fp16 arrays are numpy float16 (also only bits to the C side)."""
     if raw.dtype == np.float32:
         return ELEM_F32
     if raw.dtype == np.uint16:
         return ELEM_BF16
-    raise TypeError("oracle inputs are float32 or bf16 bits (uint16), got %s" % raw.dtype)
+    if raw.dtype == np.float16:
+        return ELEM_F16
+    raise TypeError("oracle inputs are float32, bf16 bits (uint16) or float16, got %s"
+                    % raw.dtype)
+
+
+def widen(raw: np.ndarray) -> np.ndarray:
+    """The oracle's own widening of stored elements to float64."""
+    raw = np.ascontiguousarray(raw)
+    out = np.zeros(raw.size, np.float64)
+    _load().hwkvref_widen(_ptr(raw), raw.size, elem_code(raw), _ptr(out))
+    return out.reshape(raw.shape)
 
 
 def threads() -> int:

@@ -45,17 +45,44 @@
 
 #define ELEM_F32 0
 #define ELEM_BF16 1
+#define ELEM_F16 2
+
+/* IEEE-754 binary16 to double, from the format's definition: 1 sign bit, 5
+ * exponent bits (bias 15), 10 fraction bits; exponent 0 holds zero and the
+ * subnormals (fraction * 2^-24), exponent 31 infinities and NaNs.  Every
+ * binary16 value is exact in double. */
+static double f16_to_double(uint16_t h)
+{
+    const int sign = h >> 15, ex = (h >> 10) & 0x1f, fr = h & 0x3ff;
+    double mag;
+    if (ex == 0)
+        mag = ldexp((double)fr, -24);
+    else if (ex == 31)
+        mag = fr ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + fr), ex - 25);
+    return sign ? -mag : mag;
+}
 
 /* Widen one stored element to double.  bf16 is the top half of an IEEE-754
- * binary32, so widening is exact. */
+ * binary32, so widening is exact; so is binary16. */
 static double load_elem(const void *base, int64_t idx, int elem)
 {
     if (elem == ELEM_F32)
         return (double)((const float *)base)[idx];
+    if (elem == ELEM_F16)
+        return f16_to_double(((const uint16_t *)base)[idx]);
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* The widening above, exported so that it can be checked on its own. */
+void hwkvref_widen(const void *src, int64_t n, int elem, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = load_elem(src, i, elem);
 }
 
 static int elem_size(int elem) { return elem == ELEM_F32 ? 4 : 2; }

@@ -56,12 +56,14 @@ def randn(shape, dtype: torch.dtype, generator: torch.Generator, std: float = 1.
 
 def to_raw(t: torch.Tensor) -> np.ndarray:
     """Host numpy view of a tensor's stored values: float32 stays float32,
-    bfloat16 becomes its uint16 bit patterns."""
+    bfloat16 becomes its uint16 bit patterns, float16 stays float16."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.float32:
         return t.numpy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float16:
+        return t.numpy()
     raise TypeError("unsupported dtype %s" % t.dtype)
 
 
@@ -71,6 +73,8 @@ def raw_to_f64(a: np.ndarray) -> np.ndarray:
         return a.astype(np.float64)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.float16:
+        return a.astype(np.float64)
     raise TypeError(a.dtype)
 
 

@@ -212,7 +212,7 @@ def _decode_case(dtype, n_layers, n_seqs, n_kv, G, d, T, seed):
     return q, k, v
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_decode_full_window_is_full_attention(dtype):
     n_layers, n_seqs, n_kv, G, d, T = 2, 2, 2, 3, 64, 150
     q, k, v = _decode_case(dtype, n_layers, n_seqs, n_kv, G, d, T, 11)
@@ -227,7 +227,7 @@ def test_decode_full_window_is_full_attention(dtype):
             assert np.abs(got[l, b] - ref.numpy()).max() <= 1e-12
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_decode_window_is_band_masked_attention(dtype):
     n_layers, n_seqs, n_kv, G, d, T = 2, 3, 4, 2, 32, 200
     q, k, v = _decode_case(dtype, n_layers, n_seqs, n_kv, G, d, T, 21)
@@ -240,6 +240,25 @@ def test_decode_window_is_band_masked_attention(dtype):
         for b in range(n_seqs):
             ref = _sdpa_decode(_f64(q[l, b]), _f64(k[l, b]), _f64(v[l, b]), L[b], windows[l])
             assert np.abs(got[l, b] - ref.numpy()).max() <= 1e-12
+
+
+def test_widening_of_every_16_bit_pattern_matches_the_libraries():
+    """The oracle decodes stored bf16 and fp16 bits itself (from the formats'
+    definitions); numpy's float16 and torch's bfloat16 conversions are
+    independent implementations of the same formats."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = bits.view(np.float16)
+    got = oracle.widen(f16)
+    ref = f16.astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))  # -0.0 stays -0.0
+    got = oracle.widen(bits)  # uint16 carries bf16 bits
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
 
 
 def test_decode_scale_is_applied():
@@ -266,8 +285,9 @@ def test_decode_residency_equals_masked_full_cache():
     assert np.abs(a - b).max() <= 1e-12
 
 
-def test_decode_w1_returns_newest_v_exactly():
-    q, k, v = _decode_case(torch.bfloat16, 1, 2, 2, 3, 64, 50, 41)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_decode_w1_returns_newest_v_exactly(dtype):
+    q, k, v = _decode_case(dtype, 1, 2, 2, 3, 64, 50, 41)
     L = [50, 9]
     got = oracle.decode(np.array([[1, 1]]), L, synth.to_raw(q), synth.to_raw(k),
                         synth.to_raw(v), [0, 0], 0.125)
@@ -427,7 +447,7 @@ def _raw(*ts):
     return [synth.to_raw(t) for t in ts]
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_prefill_full_window_is_causal_attention(dtype):
     n_seqs, n_kv, G, d, P, n = 2, 2, 2, 32, 45, 30
     q, kc, vc, kh, vh = _prefill_case(dtype, n_seqs, n_kv, G, d, P, n, 101)
@@ -446,7 +466,7 @@ def test_prefill_full_window_is_causal_attention(dtype):
         assert np.abs(got[b] - ref).max() <= 1e-12
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_prefill_window_is_band_masked_attention(dtype):
     n_seqs, n_kv, G, d, P, n = 2, 3, 2, 16, 50, 40
     q, kc, vc, kh, vh = _prefill_case(dtype, n_seqs, n_kv, G, d, P, n, 111)
