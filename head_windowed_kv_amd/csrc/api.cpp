@@ -164,6 +164,8 @@ static hwkv_status split_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a->n_q_heads = n_q_heads;
     a->split_tokens = L->split_tokens;
     a->rec_floats = (int32_t)record_floats(*group, L->head_dim);
+    a->tpb_log2 = 0;
+    while ((16 << a->tpb_log2) < L->block_size) a->tpb_log2++;
     a->qk_scale_log2 = scale * 1.4426950408889634f;
     return HWKV_OK;
 }

@@ -31,17 +31,24 @@
 // exponential is one v_exp_f32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "hwkv_internal.h"
 
 namespace hwkv {
 namespace {
 
-constexpr int kBS = 16;  // block_size of every supported layout
+// The kernels walk every head's window in tiles of kBS = 16 tokens.  A cache
+// block of block_size = 16 << tpb_log2 tokens holds 1 << tpb_log2 tiles.
+constexpr int kBS = 16;
+// element kinds (the values of hwkv_dtype)
+constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kEmptyMax = -1e30f;  // running max of a state that has seen no token
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16
 typedef float f32x4 __attribute__((ext_vector_type(4)));     // 4 fp32
 
@@ -51,6 +58,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                  false);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -85,22 +103,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // Element type traits: a 16-byte chunk holds EPC elements.
-template <bool BF16>
-struct Elem;
-template <>
-struct Elem<true> {
-    static constexpr int kBytes = 2;
-    typedef u32x4 Chunk;  // 8 bf16
-};
-template <>
-struct Elem<false> {
-    static constexpr int kBytes = 4;
-    typedef f32x4 Chunk;  // 4 fp32
+template <int T>
+struct Elem {
+    static constexpr int kBytes = T == kF32 ? 4 : 2;
+    typedef typename std::conditional<T == kF32, f32x4, u32x4>::type Chunk;  // 4 fp32 or 8 x 16 bit
 };
 
-template <bool BF16, int D, int G>
+template <int T, int D, int G>
 struct SplitCfg {
-    static constexpr int EB = Elem<BF16>::kBytes;
+    static constexpr int EB = Elem<T>::kBytes;
     static constexpr int ROW = D * EB;    // bytes per K (or V) row
     static constexpr int NC = ROW / 128;  // 16-byte chunks per lane per row
     static constexpr int EPC = 16 / EB;   // elements per chunk
@@ -109,61 +120,76 @@ struct SplitCfg {
     static_assert(NC >= 1 && ROW % 128 == 0, "row must be a multiple of 128 bytes");
 };
 
-// partial dot product of one row chunk with one query chunk
-__device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k, float acc) {
-    acc = dot2_bf16(q.x, k.x, acc);
-    acc = dot2_bf16(q.y, k.y, acc);
-    acc = dot2_bf16(q.z, k.z, acc);
-    acc = dot2_bf16(q.w, k.w, acc);
-    return acc;
-}
-__device__ __forceinline__ float chunk_dot(const f32x4& q, const f32x4& k, float acc) {
-    acc = fmaf(q.x, k.x, acc);
-    acc = fmaf(q.y, k.y, acc);
-    acc = fmaf(q.z, k.z, acc);
-    acc = fmaf(q.w, k.w, acc);
+// partial dot product of one row chunk with one query chunk (16-bit
+// products are exact in fp32 and accumulated in fp32)
+template <int T>
+__device__ __forceinline__ float chunk_dot(const typename Elem<T>::Chunk& q,
+                                           const typename Elem<T>::Chunk& k, float acc) {
+    if constexpr (T == kF32) {
+        acc = fmaf(q.x, k.x, acc);
+        acc = fmaf(q.y, k.y, acc);
+        acc = fmaf(q.z, k.z, acc);
+        acc = fmaf(q.w, k.w, acc);
+    } else if constexpr (T == kBF16) {
+        acc = dot2_bf16(q.x, k.x, acc);
+        acc = dot2_bf16(q.y, k.y, acc);
+        acc = dot2_bf16(q.z, k.z, acc);
+        acc = dot2_bf16(q.w, k.w, acc);
+    } else {
+        acc = dot2_f16(q.x, k.x, acc);
+        acc = dot2_f16(q.y, k.y, acc);
+        acc = dot2_f16(q.z, k.z, acc);
+        acc = dot2_f16(q.w, k.w, acc);
+    }
     return acc;
 }
 
 // widen element e of a chunk to fp32
-__device__ __forceinline__ float chunk_elem(const u32x4& v, int e) {
-    switch (e >> 1) {
-        case 0: return (e & 1) ? bf16_hi(v.x) : bf16_lo(v.x);
-        case 1: return (e & 1) ? bf16_hi(v.y) : bf16_lo(v.y);
-        case 2: return (e & 1) ? bf16_hi(v.z) : bf16_lo(v.z);
-        default: return (e & 1) ? bf16_hi(v.w) : bf16_lo(v.w);
-    }
-}
-__device__ __forceinline__ float chunk_elem(const f32x4& v, int e) {
-    switch (e) {
-        case 0: return v.x;
-        case 1: return v.y;
-        case 2: return v.z;
-        default: return v.w;
+template <int T>
+__device__ __forceinline__ float chunk_elem(const typename Elem<T>::Chunk& v, int e) {
+    if constexpr (T == kF32) {
+        switch (e) {
+            case 0: return v.x;
+            case 1: return v.y;
+            case 2: return v.z;
+            default: return v.w;
+        }
+    } else {
+        uint32_t w;
+        switch (e >> 1) {
+            case 0: w = v.x; break;
+            case 1: w = v.y; break;
+            case 2: w = v.z; break;
+            default: w = v.w; break;
+        }
+        if constexpr (T == kBF16) return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+        return (e & 1) ? f16_hi(w) : f16_lo(w);
     }
 }
 
-template <bool BF16, int D, int G>
+template <int T, int D, int G>
 struct BlockRegs {
-    typedef typename Elem<BF16>::Chunk Chunk;
-    typedef SplitCfg<BF16, D, G> C;
+    typedef typename Elem<T>::Chunk Chunk;
+    typedef SplitCfg<T, D, G> C;
     Chunk k[C::ROWS][C::NC];
     Chunk v[C::ROWS][C::NC];
 };
 
-// Issue the loads of one block for this lane (rows g + 8*rho, chunks r + 8*c).
-// Loads are unconditional: `blk` always points at a block inside the pool
-// (block 0 stands in for an invalid id), and rows outside the split are
-// masked when the block is folded in.
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void load_block(BlockRegs<BF16, D, G>& br, const uint8_t* blk, int g,
-                                           int r) {
-    typedef SplitCfg<BF16, D, G> C;
-    typedef typename Elem<BF16>::Chunk Chunk;
+// Issue the loads of one 16-token tile for this lane (rows g + 8*rho,
+// chunks r + 8*c).  `tile` points at the tile's first K row; its V rows are
+// `vofs` bytes further (block_size K rows separate a block's K and V halves).
+// Loads are unconditional: `tile` always points inside the pool (block 0
+// stands in for an invalid id), and rows outside the split are masked when
+// the tile is folded in.
+template <int T, int D, int G>
+__device__ __forceinline__ void load_block(BlockRegs<T, D, G>& br, const uint8_t* tile,
+                                           uint32_t vofs, int g, int r) {
+    typedef SplitCfg<T, D, G> C;
+    typedef typename Elem<T>::Chunk Chunk;
 #pragma unroll
     for (int rho = 0; rho < C::ROWS; rho++) {
-        const uint8_t* krow = blk + (g + 8 * rho) * C::ROW;
-        const uint8_t* vrow = krow + kBS * C::ROW;
+        const uint8_t* krow = tile + (g + 8 * rho) * C::ROW;
+        const uint8_t* vrow = krow + vofs;
 #pragma unroll
         for (int c = 0; c < C::NC; c++) {
             br.k[rho][c] =
@@ -178,13 +204,13 @@ __device__ __forceinline__ void load_block(BlockRegs<BF16, D, G>& br, const uint
 // row of the block lies in the split (the common case, no masking).
 // Otherwise row rho is used only if valid[rho]; its V chunk is zeroed so that
 // stale or uninitialised pool bytes cannot leak in as NaN * 0.
-template <bool BF16, int D, int G, bool FULL>
-__device__ __forceinline__ void process_block(BlockRegs<BF16, D, G>& br, const bool* valid,
-                                              const typename Elem<BF16>::Chunk (&qv)[G][SplitCfg<BF16, D, G>::NC],
+template <int T, int D, int G, bool FULL>
+__device__ __forceinline__ void process_block(BlockRegs<T, D, G>& br, const bool* valid,
+                                              const typename Elem<T>::Chunk (&qv)[G][SplitCfg<T, D, G>::NC],
                                               float scale_log2, float (&m)[G], float (&l)[G],
-                                              float (&acc)[G][SplitCfg<BF16, D, G>::DPL]) {
-    typedef SplitCfg<BF16, D, G> C;
-    typedef typename Elem<BF16>::Chunk Chunk;
+                                              float (&acc)[G][SplitCfg<T, D, G>::DPL]) {
+    typedef SplitCfg<T, D, G> C;
+    typedef typename Elem<T>::Chunk Chunk;
     float s[C::ROWS][G];
 #pragma unroll
     for (int rho = 0; rho < C::ROWS; rho++) {
@@ -192,7 +218,7 @@ __device__ __forceinline__ void process_block(BlockRegs<BF16, D, G>& br, const b
         for (int h = 0; h < G; h++) {
             float x = 0.f;
 #pragma unroll
-            for (int c = 0; c < C::NC; c++) x = chunk_dot(qv[h][c], br.k[rho][c], x);
+            for (int c = 0; c < C::NC; c++) x = chunk_dot<T>(qv[h][c], br.k[rho][c], x);
             x = group8_sum(x);
             s[rho][h] = (FULL || valid[rho]) ? x * scale_log2 : -INFINITY;
         }
@@ -226,7 +252,7 @@ __device__ __forceinline__ void process_block(BlockRegs<BF16, D, G>& br, const b
         for (int c = 0; c < C::NC; c++) {
 #pragma unroll
             for (int e = 0; e < C::EPC; e++) {
-                const float ve = chunk_elem(br.v[rho][c], e);
+                const float ve = chunk_elem<T>(br.v[rho][c], e);
 #pragma unroll
                 for (int h = 0; h < G; h++)
                     acc[h][c * C::EPC + e] = fmaf(p[rho][h], ve, acc[h][c * C::EPC + e]);
@@ -351,10 +377,10 @@ __device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, vo
     }
 }
 
-template <bool BF16, int D, int G, bool FUSED>
+template <int T, int D, int G, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs a) {
-    typedef SplitCfg<BF16, D, G> C;
-    typedef typename Elem<BF16>::Chunk Chunk;
+    typedef SplitCfg<T, D, G> C;
+    typedef typename Elem<T>::Chunk Chunk;
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[2 * kWaves][G];
     __shared__ float s_acc[2 * kWaves][G * D];
@@ -453,10 +479,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     const int nblk = (int)(lb1 - lb0 + 1);
     const int my_n = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
     int32_t my_id = -1;
+    const int tpb_log2 = a.tpb_log2;  // tiles per block = 1 << tpb_log2
     if (lane < my_n) {
-        const uint32_t j = (uint32_t)((lb0 + wave + (int64_t)lane * kWaves) % nb);
+        const uint32_t j = (uint32_t)(((lb0 + wave + (int64_t)lane * kWaves) >> tpb_log2) % nb);
         my_id = tbl[j];
     }
+    const uint32_t vofs = (uint32_t)(kBS << tpb_log2) * C::ROW;  // K half of a block
 
     // Fused step: the new token (position L - 1, logical block bZ) belongs to
     // the last split.  That workgroup writes its K/V rows into the ring slot
@@ -467,12 +495,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         (((int64_t)rel_layer * a.n_seqs + b) * a.n_kv_heads + hd.head) * (int64_t)C::ROW;
     if constexpr (FUSED) {
         if (new_here && wave == 0 && lane < 2 * (C::ROW / 16)) {
-            const int32_t id = tbl[(uint32_t)(bZ % nb)];
+            const int32_t id = tbl[(uint32_t)((bZ >> tpb_log2) % nb)];
             if (id >= 0 && (uint64_t)id < a.n_pool_blocks) {
                 const int half = lane / (C::ROW / 16), ch = lane % (C::ROW / 16);
+                const int64_t bs = (int64_t)kBS << tpb_log2;
                 const uint8_t* src = (half ? a.v_new : a.k_new) + kv_new_off + ch * 16;
                 uint8_t* dst = a.pool_w + (uint64_t)id * a.block_bytes +
-                               ((int64_t)half * kBS + (L - 1) % kBS) * C::ROW + ch * 16;
+                               ((int64_t)half * bs + (L - 1) % bs) * C::ROW + ch * 16;
                 *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
             }
         }
@@ -505,9 +534,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     auto block_ptr = [&](int i, bool& ok) -> const uint8_t* {
         const int32_t id = __builtin_amdgcn_readlane(my_id, i);
         ok = id >= 0 && (uint64_t)id < nblk_pool;
-        return a.pool + (uint64_t)(ok ? id : 0) * a.block_bytes;
+        const uint32_t tile_in_block =
+            (uint32_t)(lb0 + wave + (int64_t)i * kWaves) & ((1u << tpb_log2) - 1u);
+        return a.pool + (uint64_t)(ok ? id : 0) * a.block_bytes + tile_in_block * (kBS * C::ROW);
     };
-    auto fold = [&](BlockRegs<BF16, D, G>& br, int i, bool ok) {
+    auto fold = [&](BlockRegs<T, D, G>& br, int i, bool ok) {
         const int64_t lb = lb0 + wave + (int64_t)i * kWaves;
         const int64_t first = lb * kBS;
         if constexpr (FUSED) {
@@ -528,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             }
         }
         if (ok && first >= lo && first + kBS <= L) {
-            process_block<BF16, D, G, true>(br, nullptr, qv, a.qk_scale_log2, m, l, acc);
+            process_block<T, D, G, true>(br, nullptr, qv, a.qk_scale_log2, m, l, acc);
         } else {
             bool valid[C::ROWS];
 #pragma unroll
@@ -536,17 +567,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
                 const int64_t pos = first + g + 8 * rho;
                 valid[rho] = ok && pos >= lo && pos < L;
             }
-            process_block<BF16, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
+            process_block<T, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
         }
     };
 
     // Two blocks per iteration: both blocks' loads (16 KiB per wave) are
     // issued before either is folded in.
     for (int i = 0; i < my_n; i += 2) {
-        BlockRegs<BF16, D, G> bufA, bufB;
+        BlockRegs<T, D, G> bufA, bufB;
         bool okA, okB = false;
-        load_block<BF16, D, G>(bufA, block_ptr(i, okA), g, r);
-        if (i + 1 < my_n) load_block<BF16, D, G>(bufB, block_ptr(i + 1, okB), g, r);
+        load_block<T, D, G>(bufA, block_ptr(i, okA), vofs, g, r);
+        if (i + 1 < my_n) load_block<T, D, G>(bufB, block_ptr(i + 1, okB), vofs, g, r);
         fold(bufA, i, okA);
         if (i + 1 < my_n) fold(bufB, i + 1, okB);
     }
@@ -705,10 +736,10 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     }
 }
 
-template <bool BF16, int D, int G, bool FUSED>
+template <int T, int D, int G, bool FUSED>
 hwkv_status launch_split_t(const DecodeSplitArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_work_range, (unsigned)a.n_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<BF16, D, G, FUSED>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, FUSED>), grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(HWKV_ERR_HIP, std::string(FUSED ? "decode step launch: " : "decode split launch: ") +
@@ -726,14 +757,16 @@ hwkv_status launch_merge_t(const DecodeMergeArgs& a, hipStream_t s) {
     return HWKV_OK;
 }
 
-// Instances: group sizes 1..4 and 6, 8 for both dtypes and head dims.
+// Instances: group sizes 1..4 and 6, 8 for every element kind and head dim.
 #define HWKV_FOR_GROUPS(X) X(1) X(2) X(3) X(4) X(6) X(8)
 
 }  // namespace
 
 bool decode_supported(const hwkv_layout& lay, int group) {
-    if (lay.block_size != kBS) return false;
-    if (lay.dtype != HWKV_F32 && lay.dtype != HWKV_BF16) return false;
+    // block sizes: powers of two from 16 to 256 (whole 16-token tiles)
+    const int bs = lay.block_size;
+    if (bs < kBS || bs > 256 || (bs & (bs - 1)) != 0) return false;
+    if (lay.dtype != HWKV_F32 && lay.dtype != HWKV_BF16 && lay.dtype != HWKV_F16) return false;
     if (lay.head_dim != 64 && lay.head_dim != 128) return false;
     switch (group) {
         case 1: case 2: case 3: case 4: case 6: case 8: return true;
@@ -745,14 +778,17 @@ template <bool FUSED>
 hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                              hipStream_t s) {
     if (a.n_work_range <= 0) return HWKV_OK;
-    const bool bf16 = lay.dtype == HWKV_BF16;
-#define HWKV_CASE(GG)                                                                      \
-    case GG:                                                                               \
-        if (bf16)                                                                          \
-            return lay.head_dim == 128 ? launch_split_t<true, 128, GG, FUSED>(a, s)        \
-                                       : launch_split_t<true, 64, GG, FUSED>(a, s);        \
-        return lay.head_dim == 128 ? launch_split_t<false, 128, GG, FUSED>(a, s)           \
-                                   : launch_split_t<false, 64, GG, FUSED>(a, s);
+    const bool d128 = lay.head_dim == 128;
+#define HWKV_CASE(GG)                                                                        \
+    case GG:                                                                                 \
+        if (lay.dtype == HWKV_BF16)                                                          \
+            return d128 ? launch_split_t<kBF16, 128, GG, FUSED>(a, s)                        \
+                        : launch_split_t<kBF16, 64, GG, FUSED>(a, s);                        \
+        if (lay.dtype == HWKV_F16)                                                           \
+            return d128 ? launch_split_t<kF16, 128, GG, FUSED>(a, s)                         \
+                        : launch_split_t<kF16, 64, GG, FUSED>(a, s);                         \
+        return d128 ? launch_split_t<kF32, 128, GG, FUSED>(a, s)                             \
+                    : launch_split_t<kF32, 64, GG, FUSED>(a, s);
     switch (group) {
         HWKV_FOR_GROUPS(HWKV_CASE)
         default: break;

@@ -138,6 +138,7 @@ struct DecodeSplitArgs {
     int32_t layer_begin, n_seqs, n_q_heads;
     int32_t split_tokens;
     int32_t rec_floats;
+    int32_t tpb_log2;     // log2(block_size / 16): 16-token tiles per block
     float qk_scale_log2;  // scale * log2(e)
     // Fused decode step only (hwkv_decode_step): ctx_len then holds the new
     // token's position (context = position + 1); the token's K/V rows are

@@ -119,9 +119,9 @@ const char *hwkv_last_error(void);
  * blocks.  A layout is a host description: any block_size in [1, 1024],
  * head_dim in [1, 1024] and dtype F32, BF16 or F16 can be described and
  * estimated; the device calls report HWKV_ERR_UNSUPPORTED for combinations
- * that have no kernel (kernels: block_size 16; head_dim 64 or 128; decode F32
- * or BF16, prefill BF16; append any block size with rows of whole 16-byte
- * chunks).  split_tokens is the decode split length S (a multiple of
+ * that have no kernel (append: any block size, rows of whole 16-byte chunks;
+ * decode: block sizes 16, 32, 64, 128, 256, head_dim 64 or 128, F32, BF16 or
+ * F16; prefill: block size 16, head_dim 64 or 128, BF16).  split_tokens is the decode split length S (a multiple of
  * block_size, at most max(block_size, 2048); 0 picks the largest multiple of
  * block_size not above 1024).  On success *out owns the layout; free it with
  * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1, a size

@@ -14,6 +14,13 @@ import synth
 
 BF16_TOL = 2e-3
 F32_TOL = 1e-5
+# fp16 caches: inputs are exact 16-bit values and the kernels accumulate in
+# fp32 exactly as for bf16, so the bf16 gate applies
+F16_TOL = 2e-3
+
+
+def tol(dtype) -> float:
+    return F32_TOL if dtype == torch.float32 else BF16_TOL
 
 
 def say(*a):
@@ -87,7 +94,7 @@ class DecodeCase:
 
 def build_decode_case(windows, dtype, head_dim, group, ctx, seed, split_tokens=0,
                       slots=None, table_rows=None, block_ids=None, hist_margin=37,
-                      fill=0xFF, chunk=None) -> DecodeCase:
+                      fill=0xFF, chunk=None, block_size=16) -> DecodeCase:
     """Fill a cache (pool pre-filled with NaN bytes so that any read outside
     what was appended shows up) by appending each sequence's history."""
     H = hw()
@@ -95,7 +102,7 @@ def build_decode_case(windows, dtype, head_dim, group, ctx, seed, split_tokens=0
     windows = np.asarray(windows, np.int32)
     n_layers, n_kv = windows.shape
     n_seqs = len(ctx)
-    lay = H.hwkv_layout_create(windows, 16, head_dim, dtype, split_tokens)
+    lay = H.hwkv_layout_create(windows, block_size, head_dim, dtype, split_tokens)
     rows = table_rows or n_seqs
     cache = H.make_cache(lay, rows, device=dev, block_ids=block_ids, fill=fill)
     wmax = int(windows.max())
@@ -104,7 +111,7 @@ def build_decode_case(windows, dtype, head_dim, group, ctx, seed, split_tokens=0
     n_q = n_kv * group
     g = synth.gen(seed, dev)
     q = synth.randn((n_layers, n_seqs, n_q, head_dim), dtype, g, std=1.0 / math.sqrt(head_dim))
-    raw_dt = np.float32 if dtype == torch.float32 else np.uint16
+    raw_dt = {torch.float32: np.float32, torch.float16: np.float16}.get(dtype, np.uint16)
     k_hist = np.zeros((n_layers, n_seqs, T, n_kv, head_dim), raw_dt)
     v_hist = np.zeros_like(k_hist)
     k_new = torch.empty((n_layers, n_seqs, 1, n_kv, head_dim), dtype=dtype, device=dev)

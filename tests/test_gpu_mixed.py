@@ -1,0 +1,105 @@
+"""Mixed stacks through the same runtime, on the GPU, against the fp64 oracle.
+
+Covers the layouts beyond the 48-layer benchmark's: fp16 caches, block sizes
+32..256 (powers of two; the decode kernel walks 16-token tiles, so the block
+size changes only the addressing), uniform-window (sliding-window) layers,
+full-attention heads (a window longer than any context) and windows that are
+not multiples of the block size.  Bitwise gate: the same logical cache gives
+the same output bits whatever the block size and however its blocks are
+numbered."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu_common import (build_decode_case, device, hw, oracle_decode, row_rel_err,
+                         run_decode_step, say, to_host_f64, tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, out):
+    ref = oracle_decode(case)
+    got = to_host_f64(out)
+    assert np.all(np.isfinite(got))
+    err = row_rel_err(got, ref)
+    say("max row rel err", err)
+    assert err <= tol(case.dtype), err
+
+
+@pytest.mark.parametrize("d,G", [(128, 3), (64, 2), (128, 1), (64, 8), (128, 6)])
+def test_f16_decode_instances(d, G):
+    windows = [[40, 700, 1, 2100], [16, 333, 1025, 64]]
+    say("f16 decode", d, G)
+    c = build_decode_case(windows, torch.float16, d, G, [5, 900, 2500], seed=701, split_tokens=256)
+    _check(c, run_decode_step(c))
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+def test_block_sizes_match_oracle_and_block_size_16_bitwise(bs):
+    """Ragged windows (not multiples of the block size), permuted block ids,
+    sequence slots; bit-identical to the same cache built with 16-token
+    blocks (same split length, same 16-token tiles)."""
+    windows = [[1, 15, 17, 100, 513, 1500, 3000, 256], [300, 2048, 7, 4096, 600, 33, 1024, 5000]]
+    ctx = [1, 2, 17, 600, 3001, 9000]
+    slots = [5, 0, 7, 2, 1, 6]
+    say("block size", bs)
+    lay = hw().hwkv_layout_create(np.array(windows, np.int32), bs, 128, torch.bfloat16, 512)
+    bps = lay.desc().blocks_per_seq
+    perm = np.random.default_rng(bs).permutation(8 * bps).astype(np.int32).reshape(8, bps)
+    c = build_decode_case(windows, torch.bfloat16, 128, 3, ctx, seed=702, split_tokens=512,
+                          slots=slots, table_rows=8, block_ids=perm, chunk=777, block_size=bs)
+    out = run_decode_step(c)
+    _check(c, out)
+    c16 = build_decode_case(windows, torch.bfloat16, 128, 3, ctx, seed=702, split_tokens=512,
+                            slots=slots, table_rows=8, chunk=777, block_size=16)
+    assert torch.equal(out, run_decode_step(c16))
+
+
+@pytest.mark.parametrize("bs,dtype", [(32, torch.float16), (64, torch.bfloat16),
+                                      (256, torch.float32)])
+def test_fused_step_with_other_block_sizes(bs, dtype):
+    """The single-launch step writes the new token into blocks of any size:
+    output and pool equal append + decode_attn bit for bit."""
+    H = hw()
+    dev = device()
+    windows = [[64, 1000, 17], [300, 16, 2048]]
+    ctx = [2049, 16, 48, 1000]
+    mk = dict(seed=703, split_tokens=512, chunk=300, block_size=bs)
+    eager = build_decode_case(windows, dtype, 64, 2, ctx, **mk)
+    fused = build_decode_case(windows, dtype, 64, 2, ctx, **mk)
+    say("fused step, block size", bs, dtype)
+    o_e = run_decode_step(eager)
+    ws = H.make_step_workspace(fused.lay, 0, 2, len(ctx), 6, device=dev)
+    o_f = torch.full_like(o_e, float("nan"))
+    H.hwkv_decode_step(fused.cache, 0, 2, torch.tensor([x - 1 for x in ctx], device=dev),
+                       fused.k_new, fused.v_new, fused.q, 1.0 / math.sqrt(64), ws, o_f)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e, o_f)
+    assert torch.equal(eager.cache.pool, fused.cache.pool)
+    _check(fused, o_f)
+
+
+def test_mixed_stack_swa_full_and_per_head_layers():
+    """One stack: a sliding-window layer (every head the same 4096 window), a
+    full-attention layer (windows far beyond any context), a per-head layer
+    from the printed policy, and a layer of windows that are no multiple of
+    the block size; fp16 cache in 64-token blocks, four sequences."""
+    windows = [[4096] * 8, [1 << 16] * 8, list(synth.YAML_LAYER1),
+               [1000, 3, 77, 4097, 65, 129, 1, 2500]]
+    ctx = [7000, 130, 4097, 20000]
+    say("mixed stack")
+    c = build_decode_case(windows, torch.float16, 128, 3, ctx, seed=704, split_tokens=1024,
+                          block_size=64, hist_margin=20, chunk=4096)
+    _check(c, run_decode_step(c))
+
+
+def test_full_attention_layer_equals_all_tokens():
+    """A window longer than the context attends to every token: the oracle
+    (pinned against SDPA without a mask) and the kernel agree on it."""
+    c = build_decode_case([[1 << 15, 1 << 15]], torch.bfloat16, 128, 2, [3333, 17], seed=705,
+                          hist_margin=10 ** 7)
+    assert c.base == [0, 0]
+    _check(c, run_decode_step(c))
