@@ -327,6 +327,8 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a.n_q_heads = n_q_heads;
     a.n_kv_heads = L->n_kv_heads;
     a.out_bf16 = out_dtype == HWKV_BF16;
+    a.tpb_log2 = 0;
+    while ((16 << a.tpb_log2) < L->block_size) a.tpb_log2++;
     a.qk_scale_log2 = scale * 1.4426950408889634f;
     return launch_prefill(*L, group, a, stream);
 }

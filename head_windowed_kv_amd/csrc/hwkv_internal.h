@@ -187,6 +187,7 @@ struct PrefillArgs {
     void* out;
     int32_t layer, n_seqs, n_chunk, n_q_heads, n_kv_heads;
     int32_t out_bf16;
+    int32_t tpb_log2;  // log2(block_size / 16)
     float qk_scale_log2;
 };
 

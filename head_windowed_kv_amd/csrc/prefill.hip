@@ -18,8 +18,14 @@
 //                 LDS read), B = P^T taken straight from the S^T registers; the
 //                 key order of the two operands is matched through the
 //                 transpose-read addresses.
-// P is split into a bf16 high part and a bf16 remainder (two MFMAs): P rounded
-// to bf16 alone costs ~2e-3 relative error on near-uniform softmax rows.
+// bf16 caches: P is split into a bf16 high part and a bf16 remainder (two
+// MFMAs), since P rounded to bf16 alone costs ~2e-3 relative error on
+// near-uniform softmax rows.  fp16 caches use v_mfma_f32_32x32x16_f16 and one
+// PV product: P rounded to fp16 (11 significant bits) is 8x more accurate.
+//
+// Cache blocks of 16 << k tokens: every wave still stages one 16-key slice of
+// each 64-key tile; slice u of a head lives in ring block (u >> k) % nblocks,
+// at row (u mod 2^k) * 16 of that block.
 //
 // Work: a workgroup of 4 waves takes 4 consecutive "units" of one (sequence,
 // kv head); unit u is 32 consecutive query positions (u / G) of query head
@@ -44,6 +50,9 @@ constexpr float kLazy = 8.0f;  // raise the running max only when it grows by > 
 constexpr int kXcds = 8;       // MI355X dispatches workgroups round robin to 8 XCDs
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+constexpr int kBF16 = 1, kF16 = 2;  // element kinds (hwkv_dtype values)
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -88,6 +97,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// two fp32 -> packed fp16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+// 32x32x16 MFMA on 16-bit operands of element kind T, fp32 accumulation
+template <int T>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (T == kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
@@ -111,7 +135,9 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int D, int G>
+// BIG: cache blocks of more than 16 tokens (the 16-token case keeps every
+// slice address a compile-time constant)
+template <int KT, int D, int G, bool BIG>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     typedef PfCfg<D> C;
     // two stages of K and V tiles; separate objects so that the compiler sees
@@ -189,11 +215,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     auto xk = [](int j) -> uint32_t { return (uint32_t)((swz_k<D>(C::RPI * j) ) * 16); };
     const int64_t pool_blocks = (int64_t)a.n_pool_blocks;
 
+    const int tpb_log2 = BIG ? a.tpb_log2 : 0;  // 16-key slices per cache block = 1 << tpb_log2
+    const uint32_t vhalf = ((uint32_t)kBS << tpb_log2) * C::ROW;  // K half of a cache block
     auto issue = [&](uint8_t* slot_base, int64_t X, int32_t id, bool is_v) {
         uint8_t* dst = slot_base + wave * (kBS * C::ROW);
-        const int64_t tb = X * kBK + wave * kBS;  // first key of the block
+        const int64_t tb = X * kBK + wave * kBS;  // first key of the slice
+        const uint32_t sub = ((uint32_t)X * (kBK / kBS) + wave) & ((1u << tpb_log2) - 1u);
         const int64_t idc = (id >= 0 && id < pool_blocks) ? id : 0;
-        const rsrc_t rh = make_rsrc(a.pool + idc * a.block_bytes + (is_v ? kBS * C::ROW : 0),
+        const rsrc_t rh = make_rsrc(a.pool + idc * a.block_bytes +
+                                        ((is_v ? vhalf : 0u) + sub * (kBS * C::ROW)),
                                     kBS * C::ROW);
         const uint8_t* cbase = is_v ? vc_base : kc_base;
         if (tb + kBS <= P) {  // history block: every row from the ring block
@@ -226,11 +256,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             }
         }
     };
-    int32_t jw = (int32_t)((T0 * (kBK / kBS) + wave) % nb);  // ring block of the next id
+    // ring block of the next slice's id: slice u_next lives in block
+    // (u_next >> tpb_log2) % nb; successive tiles advance u by kBK / kBS
+    uint32_t u_next = (uint32_t)(T0 * (kBK / kBS) + wave);  // positions < 2^35
+    int32_t jw = (int32_t)((u_next >> tpb_log2) % (uint32_t)nb);
     auto next_id = [&]() -> int32_t {
         const int32_t id = tblc[jw];
-        jw += kBK / kBS;
+        const uint32_t u2 = u_next + kBK / kBS;
+        jw += (int32_t)((u2 >> tpb_log2) - (u_next >> tpb_log2));
         while (jw >= nb) jw -= nb;
+        u_next = u2;
         return id;
     };
 
@@ -270,8 +305,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             const uint32_t off = kx ^ (uint32_t)(32 * s);
             const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + off);
             const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + 32 * C::ROW + off);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qop[s]), s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qop[s]), s1, 0, 0, 0);
+            s0 = mfma32<KT>(a0, qop[s], s0);
+            s1 = mfma32<KT>(a1, qop[s], s1);
         }
     };
 
@@ -321,9 +356,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             const float pa = fast_exp2(fmaf(sc[kb2][r0], c2, -m_run));
             const float pb2 = fast_exp2(fmaf(sc[kb2][r0 + 1], c2, -m_run));
             const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb2);
-            hw[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-            lw[e] = pack_bf16(pa - __uint_as_float(ua & 0xffff0000u),
-                              pb2 - __uint_as_float(ub & 0xffff0000u));
+            if constexpr (KT == kF16) {
+                hw[e] = pack_f16(pa, pb2);
+                lw[e] = 0;
+            } else {
+                hw[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+                lw[e] = pack_bf16(pa - __uint_as_float(ua & 0xffff0000u),
+                                  pb2 - __uint_as_float(ub & 0xffff0000u));
+            }
             ps[e] = pa + pb2;
         }
         hi = u32x4{hw[0], hw[1], hw[2], hw[3]};
@@ -334,19 +374,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // O^T += V^T P^T for k-step ks; the V^T operands come from transpose reads
     auto pv = [&](const uint8_t* vt, int ks, const u32x4& hi, const u32x4& lo) {
         const int roff = ((ks >> 1) * 32 + (ks & 1) * 16) * C::ROW;
-        bf16x8 va[C::DBLK];
+        u32x4 va[C::DBLK];
 #pragma unroll
         for (int db = 0; db < C::DBLK; db++) {
             const u32x2 r0 = tr_read(vt + roff + vaddr[db]);
             const u32x2 r1 = tr_read(vt + roff + 8 * C::ROW + vaddr[db]);
-            va[db] = as_bf16x8(u32x4{r0.x, r0.y, r1.x, r1.y});
+            va[db] = u32x4{r0.x, r0.y, r1.x, r1.y};
         }
 #pragma unroll
-        for (int db = 0; db < C::DBLK; db++)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(hi), oacc[db], 0, 0, 0);
+        for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<KT>(va[db], hi, oacc[db]);
+        if constexpr (KT == kBF16) {
 #pragma unroll
-        for (int db = 0; db < C::DBLK; db++)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], as_bf16x8(lo), oacc[db], 0, 0, 0);
+            for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<KT>(va[db], lo, oacc[db]);
+        }
     };
 
     // ---- software pipeline over key tiles ----
@@ -437,8 +477,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
 }
 
-template <int D, int G>
+template <int T, int D, int G>
 hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
+    auto kernel = a.tpb_log2 > 0 ? prefill_kernel<T, D, G, true> : prefill_kernel<T, D, G, false>;
     const int n_pb = (a.n_chunk + kQW - 1) / kQW;
     const int n_units = G * n_pb;
     const int64_t n_groups = (n_units + kWaves - 1) / kWaves;
@@ -446,7 +487,7 @@ hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
     const int64_t blocks = (n_pairs + kXcds - 1) / kXcds * kXcds * n_groups;
     if (blocks > 0x7fffffff) return fail(HWKV_ERR_OVERFLOW, "prefill grid too large");
     dim3 grid((unsigned)blocks);
-    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(HWKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
@@ -458,8 +499,10 @@ hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
 }  // namespace
 
 bool prefill_supported(const hwkv_layout& lay, int group) {
-    if (lay.block_size != kBS) return false;
-    if (lay.dtype != HWKV_BF16 || (lay.head_dim != 64 && lay.head_dim != 128)) return false;
+    const int bs = lay.block_size;  // powers of two from 16 to 256
+    if (bs < kBS || bs > 256 || (bs & (bs - 1)) != 0) return false;
+    if (lay.dtype != HWKV_BF16 && lay.dtype != HWKV_F16) return false;
+    if (lay.head_dim != 64 && lay.head_dim != 128) return false;
     switch (group) {
         case 1: case 2: case 3: case 4: case 6: case 8: return true;
         default: return false;
@@ -469,7 +512,12 @@ bool prefill_supported(const hwkv_layout& lay, int group) {
 hwkv_status launch_prefill(const hwkv_layout& lay, int group, const PrefillArgs& a,
                            hipStream_t s) {
 #define HWKV_CASE(GG) \
-    case GG: return lay.head_dim == 128 ? launch_t<128, GG>(a, s) : launch_t<64, GG>(a, s);
+    case GG:                                                                        \
+        if (lay.dtype == HWKV_F16)                                                  \
+            return lay.head_dim == 128 ? launch_t<kF16, 128, GG>(a, s)              \
+                                       : launch_t<kF16, 64, GG>(a, s);              \
+        return lay.head_dim == 128 ? launch_t<kBF16, 128, GG>(a, s)                 \
+                                   : launch_t<kBF16, 64, GG>(a, s);
     switch (group) {
         HWKV_FOR_GROUPS(HWKV_CASE)
         default: break;

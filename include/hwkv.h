@@ -121,7 +121,7 @@ const char *hwkv_last_error(void);
  * estimated; the device calls report HWKV_ERR_UNSUPPORTED for combinations
  * that have no kernel (append: any block size, rows of whole 16-byte chunks;
  * decode: block sizes 16, 32, 64, 128, 256, head_dim 64 or 128, F32, BF16 or
- * F16; prefill: block size 16, head_dim 64 or 128, BF16).  split_tokens is the decode split length S (a multiple of
+ * F16; prefill: the same block sizes, head_dim 64 or 128, BF16 or F16).  split_tokens is the decode split length S (a multiple of
  * block_size, at most max(block_size, 2048); 0 picks the largest multiple of
  * block_size not above 1024).  On success *out owns the layout; free it with
  * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1, a size
@@ -270,8 +270,8 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * [n_seqs][n_chunk][n_kv_heads][head_dim]; out: [n_seqs][n_chunk][n_q_heads]
  * [head_dim] as out_dtype.  The cache is read, not written: call hwkv_append
  * with the same k, v (n_layers = 1) afterwards, since appending first could
- * overwrite history that earlier rows of the chunk still need.  BF16 layouts
- * with head_dim 128 use MFMA tiles. */
+ * overwrite history that earlier rows of the chunk still need.  Runs on
+ * MFMA tiles (bf16 or fp16 operands, fp32 accumulation). */
 hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer, int32_t n_seqs,
                               const int32_t *seq_slots, const int64_t *pos0,

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 class PrefillCase:
     def __init__(self, windows, d, G, pos0, n, seed, hist_keep=None, out_dtype=torch.float32,
-                 split_chunks=None):
+                 split_chunks=None, dtype=torch.bfloat16, block_size=16, block_ids=None):
         H = hw()
         dev = device()
         self.windows = np.asarray(windows, np.int32)
@@ -28,30 +28,31 @@ class PrefillCase:
         self.n_kv, self.G, self.d, self.n = n_kv, G, d, n
         self.pos0 = list(pos0)
         n_seqs = len(pos0)
-        self.lay = H.hwkv_layout_create(self.windows[None, :], 16, d, torch.bfloat16)
-        self.cache = H.make_cache(self.lay, n_seqs, device=dev, fill=0xFF)
+        self.lay = H.hwkv_layout_create(self.windows[None, :], block_size, d, dtype)
+        self.cache = H.make_cache(self.lay, n_seqs, device=dev, fill=0xFF, block_ids=block_ids)
         g = synth.gen(seed, dev)
-        cap = int(((self.windows.astype(np.int64) + 15) // 16 * 16).max())
+        bs = block_size
+        cap = int(((self.windows.astype(np.int64) + bs - 1) // bs * bs).max())
         keep = cap if hist_keep is None else hist_keep
         self.hbase = [max(0, p - keep) for p in pos0]
         Th = max(max(p - hb for p, hb in zip(pos0, self.hbase)), 1)
         self.Th = Th
-        self.k_hist = np.zeros((n_seqs, Th, n_kv, d), np.uint16)
+        raw_dt = np.float16 if dtype == torch.float16 else np.uint16
+        self.k_hist = np.zeros((n_seqs, Th, n_kv, d), raw_dt)
         self.v_hist = np.zeros_like(self.k_hist)
         for b in range(n_seqs):
             nh = pos0[b] - self.hbase[b]
             if nh == 0:
                 continue
-            kh = synth.randn((1, 1, nh, n_kv, d), torch.bfloat16, g)
-            vh = synth.randn((1, 1, nh, n_kv, d), torch.bfloat16, g)
+            kh = synth.randn((1, 1, nh, n_kv, d), dtype, g)
+            vh = synth.randn((1, 1, nh, n_kv, d), dtype, g)
             self.k_hist[b, :nh] = synth.to_raw(kh[0, 0])
             self.v_hist[b, :nh] = synth.to_raw(vh[0, 0])
             H.hwkv_append(self.cache, 0, 1, torch.tensor([self.hbase[b]], device=dev), kh, vh,
                           seq_slots=torch.tensor([b], dtype=torch.int32, device=dev))
-        self.q = synth.randn((n_seqs, n, n_kv * G, d), torch.bfloat16, g,
-                             std=1.0 / math.sqrt(d))
-        self.k = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
-        self.v = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+        self.q = synth.randn((n_seqs, n, n_kv * G, d), dtype, g, std=1.0 / math.sqrt(d))
+        self.k = synth.randn((n_seqs, n, n_kv, d), dtype, g)
+        self.v = synth.randn((n_seqs, n, n_kv, d), dtype, g)
         torch.cuda.synchronize()
 
     def run(self, out_dtype=torch.float32, scale=None):
@@ -157,3 +158,32 @@ def test_prefill_config_161k_sampled_rows():
     say("prefill 161K config: oracle on", len(rows), "rows")
     ref = c.oracle(rows=rows)
     _check(got[:, rows], ref)
+
+
+@pytest.mark.parametrize("d,G", [(128, 3), (64, 2), (128, 8)])
+def test_f16_instances(d, G):
+    """fp16 cache: fp16 MFMA tiles, P rounded once to fp16 for the PV product."""
+    say("prefill f16", d, G)
+    c = PrefillCase([300, 17, 2048, 64][:2 if G == 8 else 4], d, G, [1000, 0, 77], 333, seed=711,
+                    dtype=torch.float16)
+    _check(to_host_f64(c.run()), c.oracle())
+
+
+@pytest.mark.parametrize("bs,dtype", [(32, torch.bfloat16), (64, torch.float16),
+                                      (256, torch.bfloat16)])
+def test_other_block_sizes_with_permuted_ids(bs, dtype):
+    """Cache blocks of 32..256 tokens (each 64-key tile gathers its 16-key
+    slices from the blocks that hold them), permuted block ids, history that
+    wraps the rings; bit-identical to 16-token blocks."""
+    windows = [4096, 1000, 65, 300]
+    say("prefill block size", bs, dtype)
+    H = hw()
+    lay = H.hwkv_layout_create(np.array([windows], np.int32), bs, 128, dtype)
+    bps = lay.desc().blocks_per_seq
+    perm = np.random.default_rng(bs).permutation(2 * bps).astype(np.int32).reshape(2, bps)
+    c = PrefillCase(windows, 128, 3, [9000, 130], 400, seed=712, dtype=dtype, block_size=bs,
+                    block_ids=perm)
+    out = c.run()
+    _check(to_host_f64(out), c.oracle())
+    c16 = PrefillCase(windows, 128, 3, [9000, 130], 400, seed=712, dtype=dtype, block_size=16)
+    assert torch.equal(out, c16.run())
