@@ -37,7 +37,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=50,
+                   help="untimed steps first; the first few dozen steps after the cache fill "
+                        "run up to 6%% slower than the steady state")
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
@@ -253,11 +255,14 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
+    # one step = the split stage, which also appends each layer's new token,
+    # then the merge stage (hwkv_decode_append_attn as its two stage calls, so
+    # that the split kernel can be timed on its own)
     def run_step(i, evp=None):
-        H.hwkv_append(cache, 0, n_layers, pos[i], k_new[i], v_new[i], stream=stream)
         if evp is not None:
             evp[0].record(stream)
-        H.hwkv_decode_split(cache, 0, n_layers, ctx[i], q, scale, ws, stream=stream)
+        H.hwkv_decode_split_append(cache, 0, n_layers, pos[i], k_new[i], v_new[i], q, scale, ws,
+                                   stream=stream)
         if evp is not None:
             evp[1].record(stream)
         H.hwkv_decode_merge(cache, 0, n_layers, ctx[i], ws, out, stream=stream)
@@ -307,14 +312,15 @@ def main():
             "windows": "per (layer, head) from {1024,4096,16384,65536} p=.2/.3/.3/.2, "
                        "numpy default_rng(0)",
             "split_tokens": desc.split_tokens,
-            "launch": "one append + one split + one merge launch for all 48 layers",
+            "launch": "one split launch (which also appends the new token) + one merge launch "
+                      "for all 48 layers",
         },
         "kv_read_bytes_per_step": bytes_step,
         "kv_read_gbps": round(kv_gbps, 1),
         "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_kernel<bf16, d128, G3>",
+            "kernel": "decode_split_kernel<bf16, d128, G3, append>",
             "achieved": round(split_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -329,18 +335,21 @@ def main():
     result["practical_read_ceiling_gbps"] = round(ceiling, 1)
     result["roofline"]["frac_of_practical_ceiling"] = round(split_gbps / ceiling, 4)
 
+    result["three_launch_step"] = three_launch_leg(H, torch, cache, q, k_new, v_new,
+                                                   L0 + n_steps, n_seqs, args.steps, step_bytes,
+                                                   scale, ws, out)
     result["single_launch_step"] = fused_leg(H, torch, cache, lay, q, k_new, v_new,
-                                             L0 + n_steps, n_seqs, n_kv, G, d, args.steps,
+                                             L0 + n_steps + 32, n_seqs, n_kv, G, d, args.steps,
                                              step_bytes)
     if not args.no_graph:
-        for fused in (False, True):
+        for mode in ("three_launches", "append_in_split", "single_launch"):
             for st in (desc.split_tokens, args.graph_split_tokens):
-                key = "per_layer_graph%s_split%d" % ("_single_launch" if fused else "", st)
+                key = "per_layer_graph_%s_split%d" % (mode, st)
                 glay = lay if st == desc.split_tokens else \
                     H.hwkv_layout_create(windows, bs, d, torch.bfloat16, st)
                 result[key] = per_layer_graph(H, torch, cache, glay, windows, q, k_new, v_new,
                                               L0 + n_steps + 64, n_seqs, n_kv, G, d, step_bytes,
-                                              fused)
+                                              mode)
     if not args.no_prefill:
         del cache, ws  # the decode pool is not needed any more
         torch.cuda.empty_cache()
@@ -386,9 +395,8 @@ def cb_run(args):
     scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream()
 
-    def step(i):
-        H.hwkv_append(cache, 0, n_layers, pos[i], kn, vn)
-        H.hwkv_decode_attn(cache, 0, n_layers, ctx[i], q, scale, ws, out)
+    def step(i):  # append + attention: the split stage appends, then the merge
+        H.hwkv_decode_append_attn(cache, 0, n_layers, pos[i], kn, vn, q, scale, ws, out)
 
     step(0)
     step(1)
@@ -508,12 +516,13 @@ def prefill_leg(H, torch, synth):
 
 
 def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n_kv, G, d,
-                    step_bytes, fused=False):
+                    step_bytes, mode="three_launches"):
     """The model-realistic launch pattern: per layer append -> split -> merge
     (each layer's q only exists after the previous layer), 144 launches
     captured once in a HIP graph and replayed; positions live in device
-    scalars updated by a fill kernel outside the graph.  fused: one
-    hwkv_decode_step launch per layer instead (48 launches).  `lay` may
+    scalars updated by a fill kernel outside the graph.  mode
+    "append_in_split": hwkv_decode_append_attn per layer (96 launches);
+    "single_launch": hwkv_decode_step per layer (48 launches).  `lay` may
     differ from the cache's layout in its decode split length only (same
     windows, so the same pool geometry); its own meta blob is used."""
     dev = q.device
@@ -525,7 +534,7 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
         cache = H.Cache(lay, cache.pool, cache.block_ids, meta)
     pos = torch.full((n_seqs,), L, dtype=torch.int64, device=dev)
     ctx = torch.full((n_seqs,), L + 1, dtype=torch.int64, device=dev)
-    mk = H.make_step_workspace if fused else H.make_workspace
+    mk = H.make_step_workspace if mode == "single_launch" else H.make_workspace
     wss = [mk(lay, l, 1, n_seqs, n_kv * G, device=dev) for l in range(n_layers)]
     out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
     kn = k_new[0].clone()
@@ -539,8 +548,11 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     def layer_step(l):
-        if fused:
+        if mode == "single_launch":
             H.hwkv_decode_step(cache, l, 1, pos, kns[l], vns[l], qs[l], scale, wss[l], outs[l])
+        elif mode == "append_in_split":
+            H.hwkv_decode_append_attn(cache, l, 1, pos, kns[l], vns[l], qs[l], scale, wss[l],
+                                      outs[l])
         else:
             H.hwkv_append(cache, l, 1, pos, kns[l], vns[l])
             H.hwkv_decode_attn(cache, l, 1, ctx, qs[l], scale, wss[l], outs[l])
@@ -571,30 +583,31 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
     b = step_bytes(L + 2)
     return {"ms_per_step_median": round(ms, 4), "tokens_per_s": round(n_seqs / (ms / 1e3), 2),
             "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
-            "launches_per_step": (1 if fused else 3) * n_layers, "replays": n_rep,
+            "launches_per_step": {"single_launch": 1, "append_in_split": 2}.get(mode, 3) * n_layers,
+            "replays": n_rep,
             "split_tokens": lay.desc().split_tokens}
 
 
-def fused_leg(H, torch, cache, lay, q, k_new, v_new, L, n_seqs, n_kv, G, d, steps, step_bytes):
-    """The same decode step as one hwkv_decode_step launch for all 48 layers
-    (append, split and merge fused), timed with HIP events over `steps`
-    consecutive steps that continue the token stream."""
+def three_launch_leg(H, torch, cache, q, k_new, v_new, L, n_seqs, steps, step_bytes, scale, ws,
+                     out):
+    """The step as three launches for all 48 layers: hwkv_append of the new
+    token, then hwkv_decode_attn (split + merge)."""
     dev = q.device
     n_layers = q.shape[0]
-    ws = H.make_step_workspace(lay, 0, n_layers, n_seqs, n_kv * G, device=dev)
-    out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
     pos = [torch.full((n_seqs,), L + i, dtype=torch.int64, device=dev) for i in range(steps + 3)]
-    scale = 1.0 / math.sqrt(d)
+    ctx = [p + 1 for p in pos]
     s = torch.cuda.current_stream()
+
+    def step(i):
+        H.hwkv_append(cache, 0, n_layers, pos[i], k_new[i % len(k_new)], v_new[i % len(v_new)])
+        H.hwkv_decode_attn(cache, 0, n_layers, ctx[i], q, scale, ws, out)
     for i in range(3):
-        H.hwkv_decode_step(cache, 0, n_layers, pos[i], k_new[i % len(k_new)],
-                           v_new[i % len(v_new)], q, scale, ws, out)
+        step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for i in range(steps):
-        H.hwkv_decode_step(cache, 0, n_layers, pos[3 + i], k_new[i % len(k_new)],
-                           v_new[i % len(v_new)], q, scale, ws, out)
+        step(3 + i)
     e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -602,7 +615,42 @@ def fused_leg(H, torch, cache, lay, q, k_new, v_new, L, n_seqs, n_kv, G, d, step
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(n_seqs / (ms / 1e3), 2),
             "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
             "kv_read_frac_of_peak": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "launches_per_step": 1, "steps": steps}
+            "launches_per_step": 3, "steps": steps}
+
+
+def fused_leg(H, torch, cache, lay, q, k_new, v_new, L, n_seqs, n_kv, G, d, steps, step_bytes,
+              two_launch=False):
+    """The same decode step as one hwkv_decode_step launch for all 48 layers
+    (append, split and merge fused), or, with two_launch, as
+    hwkv_decode_append_attn (the split stage appends, then the merge), timed
+    with HIP events over `steps` consecutive steps that continue the token
+    stream."""
+    dev = q.device
+    n_layers = q.shape[0]
+    mk = H.make_workspace if two_launch else H.make_step_workspace
+    fn = H.hwkv_decode_append_attn if two_launch else H.hwkv_decode_step
+    ws = mk(lay, 0, n_layers, n_seqs, n_kv * G, device=dev)
+    out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    pos = [torch.full((n_seqs,), L + i, dtype=torch.int64, device=dev) for i in range(steps + 3)]
+    scale = 1.0 / math.sqrt(d)
+    s = torch.cuda.current_stream()
+    for i in range(3):
+        fn(cache, 0, n_layers, pos[i], k_new[i % len(k_new)], v_new[i % len(v_new)], q, scale,
+           ws, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(steps):
+        fn(cache, 0, n_layers, pos[3 + i], k_new[i % len(k_new)], v_new[i % len(v_new)], q,
+           scale, ws, out)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    b = step_bytes(L + 3)
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(n_seqs / (ms / 1e3), 2),
+            "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
+            "kv_read_frac_of_peak": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "launches_per_step": 2 if two_launch else 1, "steps": steps}
 
 
 def cpu_baseline(windows, L, n_kv, G, d, target_s, gpu_tok_s):

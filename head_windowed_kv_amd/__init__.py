@@ -40,7 +40,9 @@ EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_l
             "hwkv_layout_query", "hwkv_mem_estimate", "hwkv_capacity_check", "hwkv_table_fill",
             "hwkv_meta_fill",
             "hwkv_workspace_bytes", "hwkv_append", "hwkv_decode_split", "hwkv_decode_merge",
-            "hwkv_decode_attn", "hwkv_step_workspace_bytes", "hwkv_decode_step",
+            "hwkv_decode_attn", "hwkv_decode_split_append", "hwkv_decode_append_attn",
+            "hwkv_step_workspace_bytes",
+            "hwkv_decode_step",
             "hwkv_prefill_attn")
 
 
@@ -96,6 +98,12 @@ _lib.hwkv_decode_merge.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _
 _lib.hwkv_decode_attn.restype = ctypes.c_int
 _lib.hwkv_decode_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _i32, _vp,
                                   _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
+_lib.hwkv_decode_split_append.restype = ctypes.c_int
+_lib.hwkv_decode_split_append.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _vp,
+                                          _vp, _i32, _vp, _f32, _vp, _u64, _vp]
+_lib.hwkv_decode_append_attn.restype = ctypes.c_int
+_lib.hwkv_decode_append_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _vp,
+                                         _vp, _i32, _vp, _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
 _lib.hwkv_step_workspace_bytes.restype = ctypes.c_int
 _lib.hwkv_step_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _i32, _P(_u64)]
 _lib.hwkv_decode_step.restype = ctypes.c_int
@@ -396,14 +404,10 @@ def hwkv_decode_attn(cache: Cache, layer_begin: int, n_layers: int, ctx_len: tor
                                  _dtype_code(out.dtype), _stream(stream)))
 
 
-def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,
+def _decode_with_append(fn, cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,
                      k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, scale: float,
                      workspace: torch.Tensor, out: torch.Tensor,
                      seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Append of the token at position pos[b] and decode at context pos[b]+1
-    in one launch.  k_new, v_new: [n_layers][n_seqs][n_kv_heads][head_dim] (or
-    with a unit token axis [n_layers][n_seqs][1][n_kv_heads][head_dim]);
-    q, out: [n_layers][n_seqs][n_q_heads][head_dim]."""
     d = cache.layout.desc()
     n_seqs, n_q = int(q.shape[1]), int(q.shape[2])
     _expect("q", q, (n_layers, n_seqs, n_q, d.head_dim), torch_dtype(d.dtype))
@@ -418,10 +422,55 @@ def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.T
     _expect("pos", pos, (n_seqs,), torch.int64)
     _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
     cv = cache.view()
-    _check(_lib.hwkv_decode_step(cache.layout.handle, ctypes.byref(cv), layer_begin, n_layers,
-                                 n_seqs, _ptr(seq_slots), _ptr(pos), _ptr(k_new), _ptr(v_new),
-                                 n_q, _ptr(q), scale, _ptr(workspace), workspace.numel(),
-                                 _ptr(out), _dtype_code(out.dtype), _stream(stream)))
+    _check(fn(cache.layout.handle, ctypes.byref(cv), layer_begin, n_layers, n_seqs,
+              _ptr(seq_slots), _ptr(pos), _ptr(k_new), _ptr(v_new), n_q, _ptr(q), scale,
+              _ptr(workspace), workspace.numel(), _ptr(out), _dtype_code(out.dtype),
+              _stream(stream)))
+
+
+def hwkv_decode_split_append(cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,
+                             k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                             scale: float, workspace: torch.Tensor,
+                             seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """First stage of hwkv_decode_append_attn; follow with hwkv_decode_merge
+    at ctx_len = pos + 1."""
+    d = cache.layout.desc()
+    n_seqs, n_q = int(q.shape[1]), int(q.shape[2])
+    _expect("q", q, (n_layers, n_seqs, n_q, d.head_dim), torch_dtype(d.dtype))
+    kv_shape = (n_layers, n_seqs, d.n_kv_heads, d.head_dim)
+    if k_new.dim() == 5:
+        kv_shape = (n_layers, n_seqs, 1, d.n_kv_heads, d.head_dim)
+    _expect("k_new", k_new, kv_shape, torch_dtype(d.dtype))
+    _expect("v_new", v_new, kv_shape, torch_dtype(d.dtype))
+    _expect("pos", pos, (n_seqs,), torch.int64)
+    _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
+    cv = cache.view()
+    _check(_lib.hwkv_decode_split_append(cache.layout.handle, ctypes.byref(cv), layer_begin,
+                                         n_layers, n_seqs, _ptr(seq_slots), _ptr(pos),
+                                         _ptr(k_new), _ptr(v_new), n_q, _ptr(q), scale,
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def hwkv_decode_append_attn(cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,
+                            k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                            scale: float, workspace: torch.Tensor, out: torch.Tensor,
+                            seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append of the token at position pos[b] and decode at context pos[b]+1
+    in two launches (the split stage appends).  k_new, v_new:
+    [n_layers][n_seqs][n_kv_heads][head_dim] (or with a unit token axis);
+    q, out: [n_layers][n_seqs][n_q_heads][head_dim]; workspace: make_workspace."""
+    _decode_with_append(_lib.hwkv_decode_append_attn, cache, layer_begin, n_layers, pos, k_new,
+                        v_new, q, scale, workspace, out, seq_slots, stream)
+
+
+def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,
+                     k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, scale: float,
+                     workspace: torch.Tensor, out: torch.Tensor,
+                     seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The same step in one launch (the last split of each head merges);
+    workspace: make_step_workspace."""
+    _decode_with_append(_lib.hwkv_decode_step, cache, layer_begin, n_layers, pos, k_new, v_new,
+                        q, scale, workspace, out, seq_slots, stream)
 
 
 def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,

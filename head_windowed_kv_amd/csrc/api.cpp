@@ -203,6 +203,7 @@ static hwkv_status merge_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a->split_tokens = L->split_tokens;
     a->rec_floats = (int32_t)record_floats(*group, L->head_dim);
     a->out_bf16 = out_dtype == HWKV_BF16;
+    a->ctx_add = 0;
     return HWKV_OK;
 }
 
@@ -245,6 +246,60 @@ hwkv_status hwkv_decode_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t 
     HWKV_TRY(merge_args(L, c, layer_begin, n_layers, n_seqs, ctx_len, n_q_heads, ws, ws_bytes,
                         out, out_dtype, &group, &ma));
     HWKV_TRY(launch_decode_split(*L, group, sa, stream));
+    return launch_decode_merge(*L, group, ma, stream);
+}
+
+static hwkv_status split_append_args(const hwkv_layout* L, const hwkv_cache* c,
+                                     int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                     const int32_t* seq_slots, const int64_t* pos,
+                                     const void* k_new, const void* v_new, int32_t n_q_heads,
+                                     const void* q, float scale, void* ws, uint64_t ws_bytes,
+                                     int* group, DecodeSplitArgs* a) {
+    // pos plays the part of ctx_len (context = pos + 1) in the shared checks
+    HWKV_TRY(split_args(L, c, layer_begin, n_layers, n_seqs, seq_slots, pos, n_q_heads, q, scale,
+                        ws, ws_bytes, group, a));
+    if (!k_new || !v_new) return fail(HWKV_ERR_INVALID_ARG, "null k_new or v_new");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+        return fail(HWKV_ERR_MISALIGNED, "k_new and v_new must be 16-byte aligned");
+    a->k_new = static_cast<const uint8_t*>(k_new);
+    a->v_new = static_cast<const uint8_t*>(v_new);
+    a->pool_w = static_cast<uint8_t*>(c->pool);
+    a->n_kv_heads = L->n_kv_heads;
+    a->n_layers = n_layers;
+    return HWKV_OK;
+}
+
+hwkv_status hwkv_decode_split_append(const hwkv_layout* L, const hwkv_cache* c,
+                                     int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                     const int32_t* seq_slots, const int64_t* pos,
+                                     const void* k_new, const void* v_new, int32_t n_q_heads,
+                                     const void* q, float scale, void* ws, uint64_t ws_bytes,
+                                     hipStream_t stream) {
+    clear_error();
+    int group = 0;
+    DecodeSplitArgs sa;
+    HWKV_TRY(split_append_args(L, c, layer_begin, n_layers, n_seqs, seq_slots, pos, k_new, v_new,
+                               n_q_heads, q, scale, ws, ws_bytes, &group, &sa));
+    return launch_decode_split_append(*L, group, sa, stream);
+}
+
+hwkv_status hwkv_decode_append_attn(const hwkv_layout* L, const hwkv_cache* c,
+                                    int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                    const int32_t* seq_slots, const int64_t* pos,
+                                    const void* k_new, const void* v_new, int32_t n_q_heads,
+                                    const void* q, float scale, void* ws, uint64_t ws_bytes,
+                                    void* out, hwkv_dtype out_dtype, hipStream_t stream) {
+    clear_error();
+    int group = 0;
+    DecodeSplitArgs sa;
+    DecodeMergeArgs ma;
+    // validate both stages before enqueueing either
+    HWKV_TRY(split_append_args(L, c, layer_begin, n_layers, n_seqs, seq_slots, pos, k_new, v_new,
+                               n_q_heads, q, scale, ws, ws_bytes, &group, &sa));
+    HWKV_TRY(merge_args(L, c, layer_begin, n_layers, n_seqs, pos, n_q_heads, ws, ws_bytes, out,
+                        out_dtype, &group, &ma));
+    ma.ctx_add = 1;
+    HWKV_TRY(launch_decode_split_append(*L, group, sa, stream));
     return launch_decode_merge(*L, group, ma, stream);
 }
 

@@ -380,10 +380,17 @@ __device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, vo
     }
 }
 
-template <int T, int D, int G, bool FUSED>
+// Split-kernel modes: plain split stage; split stage that also appends the
+// new token (hwkv_decode_append_attn); the single-launch step that appends
+// and merges by the last-arriving split (hwkv_decode_step).
+constexpr int kModePlain = 0, kModeAppend = 1, kModeFused = 2;
+
+template <int T, int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs a) {
     typedef SplitCfg<T, D, G> C;
     typedef typename Elem<T>::Chunk Chunk;
+    constexpr bool FUSED = MODE == kModeFused;     // merges in the last split
+    constexpr bool APPENDS = MODE != kModePlain;  // ctx_len holds positions; appends
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[2 * kWaves][G];
     __shared__ float s_acc[2 * kWaves][G * D];
@@ -410,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     }
     const WorkItem wk = a.work[a.work_begin + blockIdx.x];
     const HeadDesc hd = a.heads[wk.head_index];
-    const int64_t L = FUSED ? a.ctx_len[b] + 1 : a.ctx_len[b];
+    const int64_t L = APPENDS ? a.ctx_len[b] + 1 : a.ctx_len[b];
     const int rel_layer = hd.layer - a.layer_begin;
     const int64_t obase =
         (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
@@ -493,10 +500,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     // the last split.  That workgroup writes its K/V rows into the ring slot
     // (the slot's previous token lies outside every window that reads the
     // block) and folds the rows from the arguments, not from the pool.
-    const bool new_here = FUSED && wk.split == ns - 1;
+    const bool new_here = APPENDS && wk.split == ns - 1;
     const int64_t kv_new_off =
         (((int64_t)rel_layer * a.n_seqs + b) * a.n_kv_heads + hd.head) * (int64_t)C::ROW;
-    if constexpr (FUSED) {
+    if constexpr (APPENDS) {
         if (new_here && wave == 0 && lane < 2 * (C::ROW / 16)) {
             const int32_t id = tbl[(uint32_t)((bZ >> tpb_log2) % nb)];
             if (id >= 0 && (uint64_t)id < a.n_pool_blocks) {
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     auto fold = [&](BlockRegs<T, D, G>& br, int i, bool ok) {
         const int64_t lb = lb0 + wave + (int64_t)i * kWaves;
         const int64_t first = lb * kBS;
-        if constexpr (FUSED) {
+        if constexpr (APPENDS) {
             if (new_here && lb == bZ) {  // the new token's row from the arguments
                 const int row = (int)((L - 1) % kBS);
 #pragma unroll
@@ -664,7 +671,7 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     auto store = [&](f32x4 o) { store_out4(a.out, a.out_bf16, obase, o); };
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
-    const int64_t L = a.ctx_len[b];
+    const int64_t L = a.ctx_len[b] + a.ctx_add;
     if (fp != a.fingerprint || L <= 0) {
         if (sg == 0) {
             const float x = fp != a.fingerprint ? __builtin_nanf("") : 0.f;
@@ -710,7 +717,7 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     const bool den_thread = (e4 * 4) % D == 0;  // first float4 of head h also sums l
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-#pragma unroll 4
+#pragma unroll 8
     for (int s = sg; s < ns; s += M::SG) {
         const float* rs = rec0 + (int64_t)s * a.rec_floats;
         const float f = fast_exp2(rs[G * D + h] - Mh);
@@ -739,13 +746,14 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     }
 }
 
-template <int T, int D, int G, bool FUSED>
+template <int T, int D, int G, int MODE>
 hwkv_status launch_split_t(const DecodeSplitArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_work_range, (unsigned)a.n_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G, FUSED>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE>), grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
-        return fail(HWKV_ERR_HIP, std::string(FUSED ? "decode step launch: " : "decode split launch: ") +
+        return fail(HWKV_ERR_HIP, std::string(MODE == kModeFused ? "decode step launch: "
+                                                                  : "decode split launch: ") +
                                       hipGetErrorString(e));
     return HWKV_OK;
 }
@@ -777,7 +785,7 @@ bool decode_supported(const hwkv_layout& lay, int group) {
     }
 }
 
-template <bool FUSED>
+template <int MODE>
 hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                              hipStream_t s) {
     if (a.n_work_range <= 0) return HWKV_OK;
@@ -785,13 +793,13 @@ hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSpli
 #define HWKV_CASE(GG)                                                                        \
     case GG:                                                                                 \
         if (lay.dtype == HWKV_BF16)                                                          \
-            return d128 ? launch_split_t<kBF16, 128, GG, FUSED>(a, s)                        \
-                        : launch_split_t<kBF16, 64, GG, FUSED>(a, s);                        \
+            return d128 ? launch_split_t<kBF16, 128, GG, MODE>(a, s)                        \
+                        : launch_split_t<kBF16, 64, GG, MODE>(a, s);                        \
         if (lay.dtype == HWKV_F16)                                                           \
-            return d128 ? launch_split_t<kF16, 128, GG, FUSED>(a, s)                         \
-                        : launch_split_t<kF16, 64, GG, FUSED>(a, s);                         \
-        return d128 ? launch_split_t<kF32, 128, GG, FUSED>(a, s)                             \
-                    : launch_split_t<kF32, 64, GG, FUSED>(a, s);
+            return d128 ? launch_split_t<kF16, 128, GG, MODE>(a, s)                         \
+                        : launch_split_t<kF16, 64, GG, MODE>(a, s);                         \
+        return d128 ? launch_split_t<kF32, 128, GG, MODE>(a, s)                             \
+                    : launch_split_t<kF32, 64, GG, MODE>(a, s);
     switch (group) {
         HWKV_FOR_GROUPS(HWKV_CASE)
         default: break;
@@ -802,12 +810,17 @@ hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSpli
 
 hwkv_status launch_decode_split(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                                 hipStream_t s) {
-    return launch_split_any<false>(lay, group, a, s);
+    return launch_split_any<kModePlain>(lay, group, a, s);
+}
+
+hwkv_status launch_decode_split_append(const hwkv_layout& lay, int group,
+                                       const DecodeSplitArgs& a, hipStream_t s) {
+    return launch_split_any<kModeAppend>(lay, group, a, s);
 }
 
 hwkv_status launch_decode_step(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                                hipStream_t s) {
-    return launch_split_any<true>(lay, group, a, s);
+    return launch_split_any<kModeFused>(lay, group, a, s);
 }
 
 hwkv_status launch_decode_merge(const hwkv_layout& lay, int group, const DecodeMergeArgs& a,

@@ -140,10 +140,11 @@ struct DecodeSplitArgs {
     int32_t rec_floats;
     int32_t tpb_log2;     // log2(block_size / 16): 16-token tiles per block
     float qk_scale_log2;  // scale * log2(e)
-    // Fused decode step only (hwkv_decode_step): ctx_len then holds the new
-    // token's position (context = position + 1); the token's K/V rows are
-    // appended by the split that covers it, and the last split of a head to
-    // finish (per-(layer, kv head, sequence) arrival counter) merges.
+    // Appending modes (hwkv_decode_append_attn, hwkv_decode_step): ctx_len
+    // then holds the new token's position (context = position + 1) and the
+    // token's K/V rows are appended by the split that covers it; in the
+    // single-launch step the last split of a head to finish (per-(layer, kv
+    // head, sequence) arrival counter) also merges.
     const uint8_t* k_new;
     const uint8_t* v_new;
     uint8_t* pool_w;
@@ -166,6 +167,7 @@ struct DecodeMergeArgs {
     int32_t split_tokens;
     int32_t rec_floats;
     int32_t out_bf16;
+    int32_t ctx_add;  // context = ctx_len[b] + ctx_add (1 when given positions)
 };
 
 struct PrefillArgs {
@@ -200,6 +202,8 @@ hwkv_status launch_prefill(const hwkv_layout& lay, int group, const PrefillArgs&
                            hipStream_t s);
 hwkv_status launch_decode_step(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                                hipStream_t s);
+hwkv_status launch_decode_split_append(const hwkv_layout& lay, int group,
+                                       const DecodeSplitArgs& a, hipStream_t s);
 
 // Whether a kernel instance exists for a layout (block size, head_dim, dtype)
 // and GQA group size.

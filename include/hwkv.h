@@ -235,6 +235,36 @@ hwkv_status hwkv_decode_attn(const hwkv_layout *layout, const hwkv_cache *cache,
                              void *workspace, uint64_t workspace_bytes, void *out,
                              hwkv_dtype out_dtype, hipStream_t stream);
 
+/* First stage of hwkv_decode_append_attn: hwkv_decode_split at context
+ * pos + 1 whose split covering the new token also writes that token's K/V
+ * rows (k_new, v_new: device [n_layers][n_seqs][n_kv_heads][head_dim]) into
+ * its ring slot and folds them from the arguments.  Follow it with
+ * hwkv_decode_merge given ctx_len = pos + 1. */
+hwkv_status hwkv_decode_split_append(const hwkv_layout *layout, const hwkv_cache *cache,
+                                     int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                     const int32_t *seq_slots, const int64_t *pos,
+                                     const void *k_new, const void *v_new,
+                                     int32_t n_q_heads, const void *q, float scale,
+                                     void *workspace, uint64_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* The effect of hwkv_append of one token at position pos[b] (k_new, v_new:
+ * device [n_layers][n_seqs][n_kv_heads][head_dim]) followed by
+ * hwkv_decode_attn with ctx_len = pos + 1, with the same results bit for bit,
+ * in two launches instead of three: the split that covers the new token
+ * writes its rows into the ring slot (the slot's previous token lies outside
+ * every window that reads the block, page 2 "SWA Window") and folds them from
+ * the arguments; the merge stage follows.  workspace: hwkv_workspace_bytes.
+ * A sequence with pos < 0 gets zeros and no append; an invalid slot gets NaN
+ * and no append. */
+hwkv_status hwkv_decode_append_attn(const hwkv_layout *layout, const hwkv_cache *cache,
+                                    int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                    const int32_t *seq_slots, const int64_t *pos,
+                                    const void *k_new, const void *v_new,
+                                    int32_t n_q_heads, const void *q, float scale,
+                                    void *workspace, uint64_t workspace_bytes, void *out,
+                                    hwkv_dtype out_dtype, hipStream_t stream);
+
 /* Device workspace of hwkv_decode_step: the hwkv_workspace_bytes records,
  * padded to 256 bytes, then one uint32 arrival counter per (layer, kv head,
  * sequence).  The counters must be zero before the first hwkv_decode_step on

@@ -21,7 +21,8 @@ from _gpu_common import (BF16_TOL, F32_TOL, build_decode_case, build_stack_case,
 pytestmark = pytest.mark.gpu
 
 
-def _fused(c, out_dtype=torch.float32, layer_begin=0, n_layers=None, scale=None, ws=None):
+def _fused(c, out_dtype=torch.float32, layer_begin=0, n_layers=None, scale=None, ws=None,
+           two_launch=False):
     H = hw()
     dev = device()
     n_layers = c.windows.shape[0] if n_layers is None else n_layers
@@ -30,14 +31,15 @@ def _fused(c, out_dtype=torch.float32, layer_begin=0, n_layers=None, scale=None,
     slots = None if c.slots is None else torch.tensor(c.slots, dtype=torch.int32, device=dev)
     pos = torch.tensor([x - 1 for x in c.ctx], dtype=torch.int64, device=dev)
     if ws is None:
-        ws = H.make_step_workspace(c.lay, layer_begin, n_layers, n_seqs, n_q, device=dev)
+        mk = H.make_workspace if two_launch else H.make_step_workspace
+        ws = mk(c.lay, layer_begin, n_layers, n_seqs, n_q, device=dev)
     out = torch.full((n_layers, n_seqs, n_q, c.head_dim), float("nan"), dtype=out_dtype,
                      device=dev)
     s = 1.0 / math.sqrt(c.head_dim) if scale is None else scale
     sl = slice(layer_begin, layer_begin + n_layers)
-    H.hwkv_decode_step(c.cache, layer_begin, n_layers, pos, c.k_new[sl].contiguous(),
-                       c.v_new[sl].contiguous(), c.q[sl].contiguous(), s, ws, out,
-                       seq_slots=slots)
+    fn = H.hwkv_decode_append_attn if two_launch else H.hwkv_decode_step
+    fn(c.cache, layer_begin, n_layers, pos, c.k_new[sl].contiguous(), c.v_new[sl].contiguous(),
+       c.q[sl].contiguous(), s, ws, out, seq_slots=slots)
     torch.cuda.synchronize()
     return out
 
@@ -56,14 +58,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("two_launch", [False, True])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_step_equals_append_then_attn(case):
+def test_step_equals_append_then_attn(case, two_launch):
+    """hwkv_decode_step (one launch) and hwkv_decode_append_attn (split stage
+    appends, then merge) against the three-call path."""
     windows, dtype, d, G, ctx, split, slots, rows = CASES[case]
-    say("fused step vs append+attn, case", case)
+    say("fused step vs append+attn, case", case, "two launches" if two_launch else "one launch")
     eager, fused = _twins(windows, dtype, d, G, ctx, seed=601 + case, split_tokens=split,
                           slots=slots, table_rows=rows, chunk=333)
     o_e = run_decode_step(eager)
-    o_f = _fused(fused)
+    o_f = _fused(fused, two_launch=two_launch)
     assert torch.equal(o_e, o_f)
     assert torch.equal(eager.cache.pool, fused.cache.pool)
     ref = oracle_decode(fused)
@@ -80,23 +85,40 @@ def test_step_bf16_output_and_layer_subrange():
     o_f = _fused(fused, out_dtype=torch.bfloat16, layer_begin=1, n_layers=2, scale=0.05)
     assert torch.equal(o_e, o_f)
     assert torch.equal(eager.cache.pool, fused.cache.pool)
+    # the two stage calls of the two-launch step: split (appending), merge
+    H = hw()
+    dev = device()
+    st = build_decode_case(windows, torch.bfloat16, 128, 3, [4500, 333], seed=611)
+    pos = torch.tensor([4499, 332], dtype=torch.int64, device=dev)
+    ws = H.make_workspace(st.lay, 1, 2, 2, 24, device=dev)
+    o_s = torch.full_like(o_e, float("nan"))
+    H.hwkv_decode_split_append(st.cache, 1, 2, pos, st.k_new[1:3].contiguous(),
+                               st.v_new[1:3].contiguous(), st.q[1:3].contiguous(), 0.05, ws)
+    H.hwkv_decode_merge(st.cache, 1, 2, pos + 1, ws, o_s)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e, o_s)
+    assert torch.equal(eager.cache.pool, st.cache.pool)
 
 
 def test_consecutive_steps_through_wraparound():
     """Eight steps in a row on one step workspace, contexts chosen so that
     windows wrap and the new token crosses block and split boundaries; every
-    step equals the two-call path bit for bit."""
+    step of both appending entry points equals the two-call path bit for
+    bit."""
     H = hw()
     dev = device()
     windows = [[16, 40, 1024, 1], [33, 256, 17, 2000]]
     ctx = [15, 1020, 2043, 250]
     eager, fused = _twins(windows, torch.bfloat16, 128, 2, ctx, seed=612, split_tokens=256)
+    two = build_decode_case(windows, torch.bfloat16, 128, 2, ctx, seed=612, split_tokens=256)
     n_layers, n_kv = 2, 4
     n_seqs, n_q = len(ctx), 8
     ws_f = H.make_step_workspace(fused.lay, 0, n_layers, n_seqs, n_q, device=dev)
     ws_e = H.make_workspace(eager.lay, 0, n_layers, n_seqs, n_q, device=dev)
+    ws_t = H.make_workspace(two.lay, 0, n_layers, n_seqs, n_q, device=dev)
     o_e = torch.empty((n_layers, n_seqs, n_q, 128), dtype=torch.float32, device=dev)
     o_f = torch.empty_like(o_e)
+    o_t = torch.empty_like(o_e)
     g = synth.gen(613, dev)
     scale = 1.0 / math.sqrt(128)
     for step in range(8):
@@ -108,9 +130,12 @@ def test_consecutive_steps_through_wraparound():
         H.hwkv_append(eager.cache, 0, n_layers, pos, k, v)
         H.hwkv_decode_attn(eager.cache, 0, n_layers, pos + 1, q, scale, ws_e, o_e)
         H.hwkv_decode_step(fused.cache, 0, n_layers, pos, k, v, q, scale, ws_f, o_f)
+        H.hwkv_decode_append_attn(two.cache, 0, n_layers, pos, k, v, q, scale, ws_t, o_t)
         torch.cuda.synchronize()
         assert torch.equal(o_e, o_f), step
+        assert torch.equal(o_e, o_t), step
         assert torch.equal(eager.cache.pool, fused.cache.pool), step
+        assert torch.equal(eager.cache.pool, two.cache.pool), step
     # the counters are back at zero after every call
     rec = H.hwkv_workspace_bytes(fused.lay, 0, n_layers, n_seqs, n_q)
     off = (rec + 255) // 256 * 256
@@ -142,6 +167,17 @@ def test_degenerate_positions_and_slots():
                        c.v_new, c.q, 1 / math.sqrt(128), ws, out)
     torch.cuda.synchronize()
     assert torch.equal(out, good)
+    # the two-launch entry point on the same degenerate inputs
+    ws2 = H.make_workspace(c.lay, 0, 1, 3, 4, device=dev)
+    out2 = torch.empty_like(out)
+    H.hwkv_decode_append_attn(c.cache, 0, 1, torch.tensor([399, -1, 399], device=dev), c.k_new,
+                              c.v_new, c.q, 1 / math.sqrt(128), ws2, out2,
+                              seq_slots=torch.tensor([0, 1, 9], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(out2[0, 0], good[0, 0])
+    assert torch.all(out2[0, 1] == 0)
+    assert torch.all(torch.isnan(out2[0, 2]))
+    assert torch.equal(c.cache.pool, pool_before)
 
 
 def test_per_layer_step_graph_replays():
