@@ -289,95 +289,142 @@ __device__ __forceinline__ void store_out4(void* out, bool bf16, int64_t at, f32
     }
 }
 
-// Merge geometry: one thread per float4 of a record's acc[G][D] (NE4 of
-// them) times SG split groups; split s is folded by group s % SG, and the SG
-// partial sums are added in a fixed order.  Many splits are read in parallel
-// instead of one after another.
+// Merge geometry.  A record's acc[G][D] is NE4 float4 columns, split into DS
+// column chunks.  A column's splits are folded by SG split groups (split s by
+// group s % SG), each in one pass with a running maximum; the SG partials are
+// then rescaled to the common maximum and added in a fixed order.  Every
+// workgroup also forms the G softmax denominators the same way.  The same
+// operations in the same order serve any grouping of chunks into workgroups
+// and the single-launch step's merge, so all give identical bits.
 template <int D, int G>
 struct MergeCfg {
     static constexpr int NE4 = G * D / 4;
-    static constexpr int SG = (1024 / NE4) < 16 ? (1024 / NE4) : 16;
-    static constexpr int THREADS = NE4 * SG;
-    static constexpr int WAVES = (THREADS + 63) / 64;
+    static constexpr int DS = NE4 >= 64 ? 4 : (NE4 >= 32 ? 2 : 1);
+    static constexpr int CPS = NE4 / DS;
+    static constexpr int SG = (2048 / NE4) < 1 ? 1 : ((2048 / NE4) > 64 ? 64 : 2048 / NE4);
+    static constexpr int PAIRS = NE4 * SG + G * SG;  // (column, group) and (head, group)
+    static constexpr int THREADS = PAIRS < 1024 ? (PAIRS + 63) / 64 * 64 : 1024;
+    static_assert(NE4 % DS == 0, "merge geometry");
 };
 
+template <bool COH>
+__device__ __forceinline__ float rec_load(const float* p) {
+    if constexpr (COH)
+        return rec_get(p);
+    else
+        return *p;
+}
+
+// factor that takes a partial kept at running maximum `from` to maximum `to`
+__device__ __forceinline__ float rescale(float from, float to) {
+    return from == to ? 1.f : fast_exp2(from - to);
+}
+
+// One pass over the splits s = k, k + SG, ... of column c (query head h):
+// running maximum m and num = sum 2^(m_s - m) acc_s[c].
+template <int D, int G, bool COH>
+__device__ __forceinline__ f32x4 merge_num_part(const float* rec0, int rec_floats, int ns, int k,
+                                                int c) {
+    typedef MergeCfg<D, G> M;
+    const int h = (c * 4) / D;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+#pragma unroll 8
+    for (int s = k; s < ns; s += M::SG) {
+        const float* rs = rec0 + (int64_t)s * rec_floats;
+        const float ms = rec_load<COH>(rs + G * D + h);
+        f32x4 v;
+        if constexpr (COH)
+            v = f32x4{rec_get(rs + c * 4), rec_get(rs + c * 4 + 1), rec_get(rs + c * 4 + 2),
+                      rec_get(rs + c * 4 + 3)};
+        else
+            v = *reinterpret_cast<const f32x4*>(rs + c * 4);
+        const float mn = fmaxf(m, ms);
+        const float al = rescale(m, mn), f = fast_exp2(ms - mn);
+        num.x = fmaf(f, v.x, num.x * al);
+        num.y = fmaf(f, v.y, num.y * al);
+        num.z = fmaf(f, v.z, num.z * al);
+        num.w = fmaf(f, v.w, num.w * al);
+        m = mn;
+    }
+    return num;
+}
+
+// The same pass for the denominator of head h: running maximum (returned in
+// m) and sum 2^(m_s - m) l_s.
+template <int D, int G, bool COH>
+__device__ __forceinline__ float merge_den_part(const float* rec0, int rec_floats, int ns, int k,
+                                                int h, float& m) {
+    typedef MergeCfg<D, G> M;
+    float den = 0.f;
+    m = -INFINITY;
+#pragma unroll 8
+    for (int s = k; s < ns; s += M::SG) {
+        const float* rs = rec0 + (int64_t)s * rec_floats;
+        const float ms = rec_load<COH>(rs + G * D + h);
+        const float ls = rec_load<COH>(rs + G * D + G + h);
+        const float mn = fmaxf(m, ms);
+        den = fmaf(fast_exp2(ms - mn), ls, den * rescale(m, mn));
+        m = mn;
+    }
+    return den;
+}
+
+// Merge of column chunks [ds0, ds1) of one (layer, sequence, kv head) by the
+// NTHREADS threads of a workgroup.  obase: output offset of the head's first
+// element.
+template <int D, int G, bool COH, int NTHREADS>
+__device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0, int ds1, void* out,
+                             bool bf16, int64_t obase) {
+    typedef MergeCfg<D, G> M;
+    __shared__ f32x4 s_num[M::SG][M::NE4];
+    __shared__ float s_den[M::SG][G];
+    __shared__ float s_mk[M::SG][G];
+    const int t = threadIdx.x;
+    const int c0 = ds0 * M::CPS, ncols = (ds1 - ds0) * M::CPS;
+    const int npairs = ncols * M::SG + G * M::SG;
+    for (int pr = t; pr < npairs; pr += NTHREADS) {
+        if (pr < ncols * M::SG) {
+            const int cl = pr % ncols, k = pr / ncols;
+            s_num[k][cl] = merge_num_part<D, G, COH>(rec0, rec_floats, ns, k, c0 + cl);
+        } else {
+            const int q = pr - ncols * M::SG;
+            const int h = q / M::SG, k = q % M::SG;
+            float m;
+            s_den[k][h] = merge_den_part<D, G, COH>(rec0, rec_floats, ns, k, h, m);
+            s_mk[k][h] = m;
+        }
+    }
+    __syncthreads();
+    for (int cl = t; cl < ncols; cl += NTHREADS) {
+        const int c = c0 + cl;
+        const int h = (c * 4) / D;
+        float Mh = s_mk[0][h];
+        for (int k = 1; k < M::SG; k++) Mh = fmaxf(Mh, s_mk[k][h]);
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+        float dtot = 0.f;
+        for (int k = 0; k < M::SG; k++) {
+            const float f = fast_exp2(s_mk[k][h] - Mh);
+            const f32x4 x = s_num[k][cl];
+            tot.x = fmaf(f, x.x, tot.x);
+            tot.y = fmaf(f, x.y, tot.y);
+            tot.z = fmaf(f, x.z, tot.z);
+            tot.w = fmaf(f, x.w, tot.w);
+            dtot = fmaf(f, s_den[k][h], dtot);
+        }
+        store_out4(out, bf16, obase + c * 4,
+                   f32x4{tot.x / dtot, tot.y / dtot, tot.z / dtot, tot.w / dtot});
+    }
+}
+
 // The merge of one (layer, sequence, kv head) done by the 256 threads of the
-// split workgroup that finished last: the same operations, in the same order,
-// as decode_merge_kernel, so both paths give identical bits.
+// split workgroup that finished last (records read with agent-coherent
+// loads): the same operations in the same order as decode_merge_kernel.
 template <int D, int G>
 __device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, void* out, bool bf16,
                                    int64_t obase) {
-    typedef MergeCfg<D, G> M;
-    constexpr int kPairs = M::NE4 * M::SG;
-    __shared__ float s_red[kWaves][G];
-    __shared__ float s_max[G];
-    __shared__ f32x4 s_num[M::SG][M::NE4];
-    __shared__ float s_den[M::SG][G];
-    const int t = threadIdx.x;
-    float mloc[G];
-#pragma unroll
-    for (int hh = 0; hh < G; hh++) mloc[hh] = -INFINITY;
-    for (int s = t; s < ns; s += kThreads) {
-#pragma unroll
-        for (int hh = 0; hh < G; hh++)
-            mloc[hh] = fmaxf(mloc[hh], rec_get(rec0 + (int64_t)s * rec_floats + G * D + hh));
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; hh++) {
-        float x = mloc[hh];
-        x = fmaxf(x, __shfl_xor(x, 32, 64));
-        x = fmaxf(x, __shfl_xor(x, 16, 64));
-        x = fmaxf(x, __shfl_xor(x, 8, 64));
-        x = fmaxf(x, __shfl_xor(x, 4, 64));
-        x = fmaxf(x, __shfl_xor(x, 2, 64));
-        x = fmaxf(x, __shfl_xor(x, 1, 64));
-        if ((t & 63) == 0) s_red[t >> 6][hh] = x;
-    }
-    __syncthreads();
-    if (t < G) {
-        float x = s_red[0][t];
-        for (int w = 1; w < kWaves; w++) x = fmaxf(x, s_red[w][t]);
-        s_max[t] = x;
-    }
-    __syncthreads();
-    for (int pr = t; pr < kPairs; pr += kThreads) {
-        const int e4 = pr % M::NE4, sg = pr / M::NE4;
-        const int h = (e4 * 4) / D;
-        const float Mh = s_max[h];
-        const bool den_thread = (e4 * 4) % D == 0;
-        f32x4 num = {0.f, 0.f, 0.f, 0.f};
-        float den = 0.f;
-#pragma unroll 4
-        for (int s = sg; s < ns; s += M::SG) {
-            const float* rs = rec0 + (int64_t)s * rec_floats;
-            const float f = fast_exp2(rec_get(rs + G * D + h) - Mh);
-            const f32x4 v = {rec_get(rs + e4 * 4), rec_get(rs + e4 * 4 + 1),
-                             rec_get(rs + e4 * 4 + 2), rec_get(rs + e4 * 4 + 3)};
-            num.x = fmaf(f, v.x, num.x);
-            num.y = fmaf(f, v.y, num.y);
-            num.z = fmaf(f, v.z, num.z);
-            num.w = fmaf(f, v.w, num.w);
-            if (den_thread) den = fmaf(f, rec_get(rs + G * D + G + h), den);
-        }
-        s_num[sg][e4] = num;
-        if (den_thread) s_den[sg][h] = den;
-    }
-    __syncthreads();
-    if (t < M::NE4) {
-        const int h = (t * 4) / D;
-        f32x4 tot = s_num[0][t];
-        float dtot = s_den[0][h];
-        for (int k = 1; k < M::SG; k++) {
-            const f32x4 x = s_num[k][t];
-            tot.x += x.x;
-            tot.y += x.y;
-            tot.z += x.z;
-            tot.w += x.w;
-            dtot += s_den[k][h];
-        }
-        store_out4(out, bf16, obase + t * 4,
-                   f32x4{tot.x / dtot, tot.y / dtot, tot.z / dtot, tot.w / dtot});
-    }
+    merge_chunks<D, G, true, kThreads>(rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, bf16,
+                                       obase);
 }
 
 // Split-kernel modes: plain split stage; split stage that also appends the
@@ -649,34 +696,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     arrive_and_merge();
 }
 
+// One workgroup per (layer, sequence, kv head) and group of a.merge_chunks
+// column chunks: all DS chunks in one workgroup when there are many heads to
+// merge, one chunk per workgroup when there are few (a single layer).
 template <int D, int G>
 __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel(DecodeMergeArgs a) {
     typedef MergeCfg<D, G> M;
-    __shared__ float s_red[M::WAVES][G];
-    __shared__ float s_max[G];
-    __shared__ f32x4 s_num[M::SG][M::NE4];
-    __shared__ float s_den[M::SG][G];
-
-    const int t = threadIdx.x;
-    const int e4 = t % M::NE4;
-    const int sg = t / M::NE4;
-    const int h = (e4 * 4) / D;  // query head (within the group) of this float4
-    const int hrel = blockIdx.x;  // kv head within the layer range
+    const int groups = M::DS / a.merge_chunks;
+    const int ds0 = (blockIdx.x % groups) * a.merge_chunks;
+    const int hrel = blockIdx.x / groups;  // kv head within the layer range
     const int b = blockIdx.y;
     const int rel_layer = hrel / a.n_kv_heads;
     const int head = hrel % a.n_kv_heads;
     const int64_t obase =
-        (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)head * G) * D + e4 * 4;
-
-    auto store = [&](f32x4 o) { store_out4(a.out, a.out_bf16, obase, o); };
+        (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)head * G) * D;
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
     const int64_t L = a.ctx_len[b] + a.ctx_add;
     if (fp != a.fingerprint || L <= 0) {
-        if (sg == 0) {
-            const float x = fp != a.fingerprint ? __builtin_nanf("") : 0.f;
-            store(f32x4{x, x, x, x});
-        }
+        const float x = fp != a.fingerprint ? __builtin_nanf("") : 0.f;
+        for (int c = ds0 * M::CPS + (int)threadIdx.x; c < (ds0 + a.merge_chunks) * M::CPS;
+             c += M::THREADS)
+            store_out4(a.out, a.out_bf16, obase + c * 4, f32x4{x, x, x, x});
         return;
     }
     const HeadDesc hd = a.heads[a.layer_begin * a.n_kv_heads + hrel];
@@ -684,66 +725,8 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     const int ns = (int)((n + a.split_tokens - 1) / a.split_tokens);
     const float* rec0 =
         a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
-
-    // running maxima of the splits, per query head
-    float mloc[G];
-#pragma unroll
-    for (int hh = 0; hh < G; hh++) mloc[hh] = -INFINITY;
-    for (int s = t; s < ns; s += M::THREADS) {
-#pragma unroll
-        for (int hh = 0; hh < G; hh++)
-            mloc[hh] = fmaxf(mloc[hh], rec0[(int64_t)s * a.rec_floats + G * D + hh]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; hh++) {
-        float x = mloc[hh];
-        x = fmaxf(x, __shfl_xor(x, 32, 64));
-        x = fmaxf(x, __shfl_xor(x, 16, 64));
-        x = fmaxf(x, __shfl_xor(x, 8, 64));
-        x = fmaxf(x, __shfl_xor(x, 4, 64));
-        x = fmaxf(x, __shfl_xor(x, 2, 64));
-        x = fmaxf(x, __shfl_xor(x, 1, 64));
-        if ((t & 63) == 0) s_red[t >> 6][hh] = x;
-    }
-    __syncthreads();
-    if (t < G) {
-        float x = s_red[0][t];
-        for (int w = 1; w < M::WAVES; w++) x = fmaxf(x, s_red[w][t]);
-        s_max[t] = x;
-    }
-    __syncthreads();
-
-    const float Mh = s_max[h];
-    const bool den_thread = (e4 * 4) % D == 0;  // first float4 of head h also sums l
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-#pragma unroll 8
-    for (int s = sg; s < ns; s += M::SG) {
-        const float* rs = rec0 + (int64_t)s * a.rec_floats;
-        const float f = fast_exp2(rs[G * D + h] - Mh);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(rs + e4 * 4);
-        num.x = fmaf(f, v.x, num.x);
-        num.y = fmaf(f, v.y, num.y);
-        num.z = fmaf(f, v.z, num.z);
-        num.w = fmaf(f, v.w, num.w);
-        if (den_thread) den = fmaf(f, rs[G * D + G + h], den);
-    }
-    s_num[sg][e4] = num;
-    if (den_thread) s_den[sg][h] = den;
-    __syncthreads();
-    if (sg == 0) {
-        f32x4 tot = s_num[0][e4];
-        float dtot = s_den[0][h];
-        for (int k = 1; k < M::SG; k++) {
-            const f32x4 x = s_num[k][e4];
-            tot.x += x.x;
-            tot.y += x.y;
-            tot.z += x.z;
-            tot.w += x.w;
-            dtot += s_den[k][h];
-        }
-        store(f32x4{tot.x / dtot, tot.y / dtot, tot.z / dtot, tot.w / dtot});
-    }
+    merge_chunks<D, G, false, M::THREADS>(rec0, ns, a.rec_floats, ds0, ds0 + a.merge_chunks, a.out,
+                                          a.out_bf16, obase);
 }
 
 template <int T, int D, int G, int MODE>
@@ -760,8 +743,13 @@ hwkv_status launch_split_t(const DecodeSplitArgs& a, hipStream_t s) {
 
 template <int D, int G>
 hwkv_status launch_merge_t(const DecodeMergeArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)(a.n_layers * a.n_kv_heads), (unsigned)a.n_seqs);
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), grid, dim3(MergeCfg<D, G>::THREADS), 0, s, a);
+    // few heads to merge (e.g. one layer): one column chunk per workgroup
+    DecodeMergeArgs b = a;
+    const int64_t heads = (int64_t)a.n_layers * a.n_kv_heads * a.n_seqs;
+    b.merge_chunks = heads >= 256 ? MergeCfg<D, G>::DS : 1;
+    const int groups = MergeCfg<D, G>::DS / b.merge_chunks;
+    dim3 grid((unsigned)(a.n_layers * a.n_kv_heads * groups), (unsigned)a.n_seqs);
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), grid, dim3(MergeCfg<D, G>::THREADS), 0, s, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(HWKV_ERR_HIP, std::string("decode merge launch: ") + hipGetErrorString(e));

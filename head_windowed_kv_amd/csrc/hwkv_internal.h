@@ -168,6 +168,7 @@ struct DecodeMergeArgs {
     int32_t rec_floats;
     int32_t out_bf16;
     int32_t ctx_add;  // context = ctx_len[b] + ctx_add (1 when given positions)
+    int32_t merge_chunks;  // column chunks per workgroup (set by the launcher)
 };
 
 struct PrefillArgs {
