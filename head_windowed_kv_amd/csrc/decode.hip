@@ -79,11 +79,16 @@ __device__ __forceinline__ float dpp(float x) {
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 8 lanes of a group; every lane of the group gets the sum.
-__device__ __forceinline__ float group8_sum(float x) {
+// Sum over the N (8, 16 or 32) lanes of a group; every lane of the group
+// gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
     x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: pairs
     x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: quads
     x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+    if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror: the other 8 of the 16
+    if constexpr (N >= 32)
+        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // ^16
     return x;
 }
 
@@ -112,12 +117,16 @@ struct Elem {
 template <int T, int D, int G>
 struct SplitCfg {
     static constexpr int EB = Elem<T>::kBytes;
-    static constexpr int ROW = D * EB;    // bytes per K (or V) row
-    static constexpr int NC = ROW / 128;  // 16-byte chunks per lane per row
-    static constexpr int EPC = 16 / EB;   // elements per chunk
-    static constexpr int DPL = NC * EPC;  // dims owned per lane
-    static constexpr int ROWS = kBS / 8;  // rows per group per block
-    static_assert(NC >= 1 && ROW % 128 == 0, "row must be a multiple of 128 bytes");
+    static constexpr int ROW = D * EB;  // bytes per K (or V) row
+    // lanes per row group: 8 for rows up to 256 bytes, 32 for 512-byte rows
+    // (the accumulator of a lane then holds 8 elements per query head)
+    static constexpr int LPG = ROW >= 512 ? 32 : 8;
+    static constexpr int NC = ROW / (16 * LPG);  // 16-byte chunks per lane per row
+    static constexpr int EPC = 16 / EB;          // elements per chunk
+    static constexpr int DPL = NC * EPC;         // dims owned per lane
+    static constexpr int NG = 64 / LPG;          // row groups per wave
+    static constexpr int ROWS = kBS / NG;        // rows per group per tile
+    static_assert(NC >= 1 && ROW % (16 * LPG) == 0, "rows of whole lane chunks");
 };
 
 // partial dot product of one row chunk with one query chunk (16-bit
@@ -188,14 +197,14 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D, G>& br, const uint8_t
     typedef typename Elem<T>::Chunk Chunk;
 #pragma unroll
     for (int rho = 0; rho < C::ROWS; rho++) {
-        const uint8_t* krow = tile + (g + 8 * rho) * C::ROW;
+        const uint8_t* krow = tile + (g + C::NG * rho) * C::ROW;
         const uint8_t* vrow = krow + vofs;
 #pragma unroll
         for (int c = 0; c < C::NC; c++) {
             br.k[rho][c] =
-                __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(krow + (c * 8 + r) * 16));
+                __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(krow + (c * C::LPG + r) * 16));
             br.v[rho][c] =
-                __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vrow + (c * 8 + r) * 16));
+                __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(vrow + (c * C::LPG + r) * 16));
         }
     }
 }
@@ -219,7 +228,7 @@ __device__ __forceinline__ void process_block(BlockRegs<T, D, G>& br, const bool
             float x = 0.f;
 #pragma unroll
             for (int c = 0; c < C::NC; c++) x = chunk_dot<T>(qv[h][c], br.k[rho][c], x);
-            x = group8_sum(x);
+            x = group_sum<C::LPG>(x);
             s[rho][h] = (FULL || valid[rho]) ? x * scale_log2 : -INFINITY;
         }
         if (!FULL && !valid[rho]) {
@@ -444,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int r = lane & 7;
-    const int g = lane >> 3;
+    const int r = lane % C::LPG;  // chunks r, r + LPG, ... of a row
+    const int g = lane / C::LPG;  // rows g, g + NG, ... of every tile
     const int b = blockIdx.y;
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
@@ -574,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         for (int h = 0; h < G; h++)
 #pragma unroll
             for (int c = 0; c < C::NC; c++)
-                qv[h][c] = *reinterpret_cast<const Chunk*>(qb + (h * D) * C::EB + (c * 8 + r) * 16);
+                qv[h][c] = *reinterpret_cast<const Chunk*>(qb + (h * D) * C::EB + (c * C::LPG + r) * 16);
     }
 
     float m[G], l[G], acc[G][C::DPL];
@@ -603,13 +612,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
                 const int row = (int)((L - 1) % kBS);
 #pragma unroll
                 for (int rho = 0; rho < C::ROWS; rho++) {
-                    if (g + 8 * rho == row) {
+                    if (g + C::NG * rho == row) {
 #pragma unroll
                         for (int c = 0; c < C::NC; c++) {
-                            br.k[rho][c] = *reinterpret_cast<const Chunk*>(a.k_new + kv_new_off +
-                                                                           (c * 8 + r) * 16);
-                            br.v[rho][c] = *reinterpret_cast<const Chunk*>(a.v_new + kv_new_off +
-                                                                           (c * 8 + r) * 16);
+                            br.k[rho][c] = *reinterpret_cast<const Chunk*>(
+                                a.k_new + kv_new_off + (c * C::LPG + r) * 16);
+                            br.v[rho][c] = *reinterpret_cast<const Chunk*>(
+                                a.v_new + kv_new_off + (c * C::LPG + r) * 16);
                         }
                     }
                 }
@@ -621,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             bool valid[C::ROWS];
 #pragma unroll
             for (int rho = 0; rho < C::ROWS; rho++) {
-                const int64_t pos = first + g + 8 * rho;
+                const int64_t pos = first + g + C::NG * rho;
                 valid[rho] = ok && pos >= lo && pos < L;
             }
             process_block<T, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
@@ -643,8 +652,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 #pragma unroll
     for (int h = 0; h < G; h++) {
         float M = m[h];
-        M = fmaxf(M, xor8(M));
-        M = fmaxf(M, xor16(M));
+        if constexpr (C::LPG <= 8) M = fmaxf(M, xor8(M));
+        if constexpr (C::LPG <= 16) M = fmaxf(M, xor16(M));
         M = fmaxf(M, xor32(M));
         if (lane == 0) s_m[wave][h] = M;
     }
@@ -656,22 +665,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
         const float f = fast_exp2(m[h] - MW);
         float lh = l[h] * f;
-        lh += xor8(lh);
-        lh += xor16(lh);
+        if constexpr (C::LPG <= 8) lh += xor8(lh);
+        if constexpr (C::LPG <= 16) lh += xor16(lh);
 #pragma unroll
         for (int i = 0; i < C::DPL; i++) {
             float x = acc[h][i] * f;
-            x += xor8(x);
-            x += xor16(x);
+            if constexpr (C::LPG <= 8) x += xor8(x);
+            if constexpr (C::LPG <= 16) x += xor16(x);
             acc[h][i] = x;
         }
-        if ((g & 3) == 0) {  // groups 0 and 4 hold the two half-wave sums
-            const int sl = wave * 2 + (g >> 2);
+        if ((lane & 31) < C::LPG) {  // the first group of each half wave holds its sums
+            const int sl = wave * 2 + (lane >> 5);
 #pragma unroll
             for (int c = 0; c < C::NC; c++)
 #pragma unroll
                 for (int e = 0; e < C::EPC; e++)
-                    s_acc[sl][h * D + (c * 8 + r) * C::EPC + e] = acc[h][c * C::EPC + e];
+                    s_acc[sl][h * D + (c * C::LPG + r) * C::EPC + e] = acc[h][c * C::EPC + e];
             if (r == 0) s_l[sl][h] = lh;
         }
     }
@@ -766,7 +775,8 @@ bool decode_supported(const hwkv_layout& lay, int group) {
     const int bs = lay.block_size;
     if (bs < kBS || bs > 256 || (bs & (bs - 1)) != 0) return false;
     if (lay.dtype != HWKV_F32 && lay.dtype != HWKV_BF16 && lay.dtype != HWKV_F16) return false;
-    if (lay.head_dim != 64 && lay.head_dim != 128) return false;
+    if (lay.head_dim != 64 && lay.head_dim != 128 && lay.head_dim != 256) return false;
+    if (lay.head_dim == 256 && (lay.dtype == HWKV_F32 || group > 4)) return false;
     switch (group) {
         case 1: case 2: case 3: case 4: case 6: case 8: return true;
         default: return false;
@@ -777,6 +787,20 @@ template <int MODE>
 hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                              hipStream_t s) {
     if (a.n_work_range <= 0) return HWKV_OK;
+    if (lay.head_dim == 256) {  // 16-bit caches, groups up to 4
+        const bool f16 = lay.dtype == HWKV_F16;
+#define HWKV_CASE256(GG)                                                                     \
+    case GG:                                                                                 \
+        return f16 ? launch_split_t<kF16, 256, GG, MODE>(a, s)                               \
+                   : launch_split_t<kBF16, 256, GG, MODE>(a, s);
+        switch (group) {
+            HWKV_CASE256(1) HWKV_CASE256(2) HWKV_CASE256(3) HWKV_CASE256(4)
+            default: break;
+        }
+#undef HWKV_CASE256
+        return fail(HWKV_ERR_UNSUPPORTED, "no head_dim 256 decode kernel for GQA group " +
+                                              std::to_string(group));
+    }
     const bool d128 = lay.head_dim == 128;
 #define HWKV_CASE(GG)                                                                        \
     case GG:                                                                                 \
@@ -813,6 +837,17 @@ hwkv_status launch_decode_step(const hwkv_layout& lay, int group, const DecodeSp
 
 hwkv_status launch_decode_merge(const hwkv_layout& lay, int group, const DecodeMergeArgs& a,
                                 hipStream_t s) {
+    if (lay.head_dim == 256) {
+        switch (group) {
+            case 1: return launch_merge_t<256, 1>(a, s);
+            case 2: return launch_merge_t<256, 2>(a, s);
+            case 3: return launch_merge_t<256, 3>(a, s);
+            case 4: return launch_merge_t<256, 4>(a, s);
+            default: break;
+        }
+        return fail(HWKV_ERR_UNSUPPORTED, "no head_dim 256 merge kernel for GQA group " +
+                                              std::to_string(group));
+    }
 #define HWKV_CASE(GG)                                                                        \
     case GG:                                                                                 \
         return lay.head_dim == 128 ? launch_merge_t<128, GG>(a, s) : launch_merge_t<64, GG>(a, s);

@@ -178,6 +178,8 @@ def _unsupported_calls(lay, group):
     (48, 128, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (512, 64, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (16, 96, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+    (16, 256, "bf16", ["ok", "ok", "HWKV_ERR_UNSUPPORTED"]),
+    (16, 256, "f32", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (16, 4, "bf16", ["HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
 ])
 def test_device_calls_without_a_kernel_are_rejected_before_launch(bs, d, dt, want):
