@@ -43,9 +43,12 @@ def parse():
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
-    p.add_argument("--graph-split-tokens", type=int, default=256,
-                   help="decode split length of the second per-layer graph variant")
+    p.add_argument("--graph-split-tokens", type=int, default=384,
+                   help="decode split length of the second per-layer graph variant (384 is "
+                        "the fastest per-layer split measured from 128 to 1024)")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="run only the 161K chunked-prefill leg (e.g. under rocprofv3 --pmc)")
     p.add_argument("--config", choices=("stack48", "cb"), default="stack48",
                    help="stack48: the 48-layer 112K decode step (default, the headline line); "
                         "cb: the 32-sequence continuous batch, 256 steps (138 GB pool)")
@@ -203,6 +206,14 @@ def main():
         sys.exit(2)
     if args.config == "cb":
         cb_run(args)
+        return
+    if args.prefill_only:
+        import torch
+
+        import head_windowed_kv_amd as H
+        import synth
+        torch.cuda.set_device(0)
+        print(json.dumps({"prefill_161k": prefill_leg(H, torch, synth)}), flush=True)
         return
 
     import numpy as np

@@ -167,6 +167,7 @@ static hwkv_status split_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a->tpb_log2 = 0;
     while ((16 << a->tpb_log2) < L->block_size) a->tpb_log2++;
     a->qk_scale_log2 = scale * 1.4426950408889634f;
+    a->rec_streamed = (int64_t)a->n_work_range * n_seqs >= kStreamedRecordsMinWorkgroups;
     return HWKV_OK;
 }
 

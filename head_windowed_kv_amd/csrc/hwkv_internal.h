@@ -14,6 +14,9 @@ namespace hwkv {
 constexpr uint32_t kMetaMagic = 0x564B5748u;  // "HWKV"
 constexpr int kDefaultSplitTokens = 1024;
 constexpr int kMaxSplitTokens = 2048;
+// Split launches of at least this many workgroups write their records with
+// non-temporal stores (see rec_put in decode.hip).
+constexpr int64_t kStreamedRecordsMinWorkgroups = 2048;
 constexpr int kMaxBlockSize = 1024;
 constexpr int kMaxHeadDim = 1024;
 
@@ -140,6 +143,10 @@ struct DecodeSplitArgs {
     int32_t rec_floats;
     int32_t tpb_log2;     // log2(block_size / 16): 16-token tiles per block
     float qk_scale_log2;  // scale * log2(e)
+    // 1: records are written with non-temporal stores (launches long enough
+    // that their write-back would compete with the K/V read stream); 0:
+    // ordinary stores, which the merge stage reads back sooner
+    int32_t rec_streamed;
     // Appending modes (hwkv_decode_append_attn, hwkv_decode_step): ctx_len
     // then holds the new token's position (context = position + 1) and the
     // token's K/V rows are appended by the split that covers it; in the
