@@ -440,6 +440,27 @@ def cb_run(args):
     print(json.dumps(res), flush=True)
 
 
+def gemm_reference_tflops(torch, n=16384, reps=5):
+    """Practical bf16 matrix-core rate on this machine: a plain n x n x n bf16
+    GEMM from the vendor library (torch.matmul), timed with HIP events.  A
+    reference point for the prefill's MFMA fraction (the way the streaming
+    read probe is one for decode), not part of the measured path."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms / 1e3) / 1e12
+
+
 def prefill_leg(H, torch, synth):
     """Chunked prefill at 161K context: 4 sequences, 8 KV heads x 3, d=128,
     bf16, windows of the printed policy's layer 0 (4096 x2, 16384 x2, 65536
@@ -515,11 +536,16 @@ def prefill_leg(H, torch, synth):
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1) / n_dec
     dec_bytes = float(np.minimum(w.astype(np.int64), P + n).sum()) * n_seqs * KV_BYTES_PER_TOK_HEAD
+    del cache
+    torch.cuda.empty_cache()
+    gemm_tf = gemm_reference_tflops(torch)
     return {"workload": "4 seqs x 1 layer, 2048-token chunk at P=164864, windows 4096x2/16384x2/"
                         "65536x4, 8x3 heads, d=128, bf16",
             "prefill_ms": round(pf_ms, 4), "prefill_flop": flop,
             "prefill_tflops": round(flop / (pf_ms / 1e3) / 1e12, 1),
             "mfma_frac_of_bf16_peak": round(flop / (pf_ms / 1e3) / 2.5e15, 4),
+            "gemm_reference_tflops": round(gemm_tf, 1),
+            "frac_of_gemm_reference": round(flop / (pf_ms / 1e3) / 1e12 / gemm_tf, 4),
             "prefill_tokens_per_s": round(n_seqs * n / (pf_ms / 1e3), 1),
             "chunk_append_ms": round(append_ms, 4),
             "decode_step_ms": round(dec_ms, 4),
