@@ -234,9 +234,10 @@ def test_per_layer_step_graph_replays():
 
 def test_stack48_step_full_size():
     """The 48-layer 112K stack (windows from {1K,4K,16K,64K}, seed 0, batch 1):
-    the single-launch step equals the append + split + merge launches bit for
-    bit over every output row and the whole pool, and sampled layers match
-    the oracle."""
+    the single-launch step and the two-launch step (the split stage appends;
+    the benchmark's headline launches) equal the append + split + merge
+    launches bit for bit over every output row and the whole pool, and
+    sampled layers match the oracle."""
     H = hw()
     dev = device()
     w = synth.stack_windows(48, 8, 0)
@@ -245,16 +246,57 @@ def test_stack48_step_full_size():
     f = build_stack_case(w, torch.bfloat16, 128, 3, synth.CTX_112K, 1, seed=103)
     say("stack48 fused: steps")
     o_e = stack_step(e)
+    pos = torch.tensor([synth.CTX_112K], device=dev)
     ws = H.make_step_workspace(f.lay, 0, 48, 1, 24, device=dev)
     o_f = torch.full_like(o_e, float("nan"))
-    H.hwkv_decode_step(f.cache, 0, 48, torch.tensor([synth.CTX_112K], device=dev), f.k_new,
-                       f.v_new, f.q, 1.0 / math.sqrt(128), ws, o_f)
+    H.hwkv_decode_step(f.cache, 0, 48, pos, f.k_new, f.v_new, f.q, 1.0 / math.sqrt(128), ws, o_f)
     torch.cuda.synchronize()
     assert torch.equal(o_e, o_f)
     assert torch.equal(e.cache.pool, f.cache.pool)
+    say("stack48 two launches: fill and step")
+    del e
+    torch.cuda.empty_cache()
+    t = build_stack_case(w, torch.bfloat16, 128, 3, synth.CTX_112K, 1, seed=103)
+    ws2 = H.make_workspace(t.lay, 0, 48, 1, 24, device=dev)
+    o_t = torch.full_like(o_e, float("nan"))
+    H.hwkv_decode_append_attn(t.cache, 0, 48, pos, t.k_new, t.v_new, t.q, 1.0 / math.sqrt(128),
+                              ws2, o_t)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e, o_t)
+    assert torch.equal(t.cache.pool, f.cache.pool)
+    del t
     got = to_host_f64(o_f)
     worst = 0.0
     for l in (0, 17, 47):
         worst = max(worst, row_rel_err(got[l:l + 1], stack_oracle_layer(f, l)))
     say("stack48 fused max row rel err (sampled layers)", worst)
+    assert worst <= BF16_TOL
+
+
+def test_stack48_per_layer_split384():
+    """The per-layer launch pattern of the benchmark's graph legs on the
+    48-layer 112K stack: decode split length 384, one two-launch step
+    (appending split + merge) per layer; sampled layers against the oracle."""
+    H = hw()
+    dev = device()
+    w = synth.stack_windows(48, 8, 0)
+    say("stack48 per layer split 384: fill")
+    c = build_stack_case(w, torch.bfloat16, 128, 3, synth.CTX_112K, 1, seed=103,
+                         split_tokens=384)
+    assert c.lay.desc().split_tokens == 384
+    pos = torch.tensor([synth.CTX_112K], device=dev)
+    out = torch.full((48, 1, 24, 128), float("nan"), dtype=torch.float32, device=dev)
+    say("stack48 per layer split 384: 48 steps")
+    for l in range(48):
+        ws = H.make_workspace(c.lay, l, 1, 1, 24, device=dev)
+        H.hwkv_decode_append_attn(c.cache, l, 1, pos, c.k_new[l:l + 1].contiguous(),
+                                  c.v_new[l:l + 1].contiguous(), c.q[l:l + 1].contiguous(),
+                                  1.0 / math.sqrt(128), ws, out[l:l + 1])
+    torch.cuda.synchronize()
+    got = to_host_f64(out)
+    assert np.all(np.isfinite(got))
+    worst = 0.0
+    for l in (0, 5, 17, 31, 47):
+        worst = max(worst, row_rel_err(got[l:l + 1], stack_oracle_layer(c, l)))
+    say("stack48 per layer split 384 max row rel err (sampled layers)", worst)
     assert worst <= BF16_TOL
