@@ -23,6 +23,9 @@
 // near-uniform softmax rows.  fp16 caches use v_mfma_f32_32x32x16_f16 and one
 // PV product: P rounded to fp16 (11 significant bits) is 8x more accurate.
 //
+// head_dim 256: the accumulators and query operands take twice the registers
+// (484 VGPRs), so that instance runs one wave per SIMD, with 32 KiB tiles.
+//
 // Cache blocks of 16 << k tokens: every wave still stages one 16-key slice of
 // each 64-key tile; slice u of a head lives in ring block (u >> k) % nblocks,
 // at row (u mod 2^k) * 16 of that block.
@@ -30,9 +33,11 @@
 // Work: a workgroup of 4 waves takes 4 consecutive "units" of one (sequence,
 // kv head); unit u is 32 consecutive query positions (u / G) of query head
 // (u % G), so the G heads of a GQA group share every K/V tile.  Key tiles of
-// 64 positions are staged through LDS (double buffered, rows padded against
-// bank conflicts); a wave skips the MFMAs of tiles outside its own band and
-// masks only tiles that cross its window start or its causal diagonal.
+// 64 positions are staged through LDS (double buffered, 16-byte chunks
+// swizzled against bank conflicts); every wave runs the workgroup's key range
+// (the union of its units' windows, at most a tile or two wider than its
+// own) and masks only the tiles that cross its window start or its causal
+// diagonal.
 #include <hip/hip_runtime.h>
 
 #include "hwkv_internal.h"
@@ -79,11 +84,11 @@ struct PfCfg {
 // reads 32 bytes of 4 consecutive rows.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+    return D >= 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-    return D == 128 ? 2 * ((2 * (r & 3)) ^ ((r >> 1) & 1)) : 2 * (r & 3);
+    return D >= 128 ? 2 * ((2 * (r & 3)) ^ ((r >> 1) & 1)) : 2 * (r & 3);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -138,7 +143,7 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, ui
 // BIG: cache blocks of more than 16 tokens (the 16-token case keeps every
 // slice address a compile-time constant)
 template <int KT, int D, int G, bool BIG>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(PrefillArgs a) {
     typedef PfCfg<D> C;
     // two stages of K and V tiles; separate objects so that the compiler sees
     // that a DMA into one stage never aliases the reads of the other
@@ -211,8 +216,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const uint32_t cv = (uint32_t)((la ^ swz_v<D>(lq)) * 16);
     const uint32_t hK = (uint32_t)(lq * C::ROW) + ck, hV = (uint32_t)(lq * C::ROW) + cv;
     const uint32_t cK = (uint32_t)(lq * stride) + ck, cV = (uint32_t)(lq * stride) + cv;
-    // the K swizzle of row RPI j + lq differs from that of row lq by xk(j)
+    // the K (V) swizzle of row RPI j + lq differs from that of row lq by
+    // xk(j) (xv(j)); xv is zero unless a DMA instruction covers fewer than 4 rows
     auto xk = [](int j) -> uint32_t { return (uint32_t)((swz_k<D>(C::RPI * j) ) * 16); };
+    auto xv = [](int j) -> uint32_t { return (uint32_t)((swz_v<D>(C::RPI * j) ) * 16); };
     const int64_t pool_blocks = (int64_t)a.n_pool_blocks;
 
     const int tpb_log2 = BIG ? a.tpb_log2 : 0;  // 16-key slices per cache block = 1 << tpb_log2
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         if (tb + kBS <= P) {  // history block: every row from the ring block
 #pragma unroll
             for (int j = 0; j < C::NI; j++)
-                dma16(rh, is_v ? hV : (hK ^ xk(j)), j * 1024, dst + j * 1024);
+                dma16(rh, is_v ? (hV ^ xv(j)) : (hK ^ xk(j)), j * 1024, dst + j * 1024);
         } else if (tb >= P) {
             // rows of the chunk's own k, v; rows past the chunk end read as
             // zero (no query attends to them)
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             const rsrc_t rc = make_rsrc(cbase + r0 * stride, (uint32_t)(rows * stride));
 #pragma unroll
             for (int j = 0; j < C::NI; j++)
-                dma16(rc, (uint32_t)(j * C::RPI * stride) + (is_v ? cV : (cK ^ xk(j))), 0,
+                dma16(rc, (uint32_t)(j * C::RPI * stride) + (is_v ? (cV ^ xv(j)) : (cK ^ xk(j))), 0,
                       dst + j * 1024);
         } else {
             // the block that holds the chunk start: rows before it from the
@@ -248,9 +255,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int j = 0; j < C::NI; j++) {
                 const int64_t t = tb + C::RPI * j + lq;
-                const uint32_t cpart = is_v ? cv : (ck ^ xk(j));
+                const uint32_t cpart = is_v ? (cv ^ xv(j)) : (ck ^ xk(j));
                 if (t < P)
-                    dma16(rh, is_v ? hV : (hK ^ xk(j)), j * 1024, dst + j * 1024);
+                    dma16(rh, is_v ? (hV ^ xv(j)) : (hK ^ xk(j)), j * 1024, dst + j * 1024);
                 else
                     dma16(rc, (uint32_t)((t - P) * stride) + cpart, 0, dst + j * 1024);
             }
@@ -502,15 +509,29 @@ bool prefill_supported(const hwkv_layout& lay, int group) {
     const int bs = lay.block_size;  // powers of two from 16 to 256
     if (bs < kBS || bs > 256 || (bs & (bs - 1)) != 0) return false;
     if (lay.dtype != HWKV_BF16 && lay.dtype != HWKV_F16) return false;
-    if (lay.head_dim != 64 && lay.head_dim != 128) return false;
+    if (lay.head_dim != 64 && lay.head_dim != 128 && lay.head_dim != 256) return false;
     switch (group) {
-        case 1: case 2: case 3: case 4: case 6: case 8: return true;
+        case 1: case 2: case 3: case 4: return true;
+        case 6: case 8: return lay.head_dim != 256;
         default: return false;
     }
 }
 
 hwkv_status launch_prefill(const hwkv_layout& lay, int group, const PrefillArgs& a,
                            hipStream_t s) {
+    if (lay.head_dim == 256) {  // groups 1 to 4; one wave per SIMD (see the header)
+#define HWKV_CASE256(GG)                                                                     \
+    case GG:                                                                                 \
+        return lay.dtype == HWKV_F16 ? launch_t<kF16, 256, GG>(a, s)                         \
+                                     : launch_t<kBF16, 256, GG>(a, s);
+        switch (group) {
+            HWKV_CASE256(1) HWKV_CASE256(2) HWKV_CASE256(3) HWKV_CASE256(4)
+            default: break;
+        }
+#undef HWKV_CASE256
+        return fail(HWKV_ERR_UNSUPPORTED,
+                    "no head_dim 256 prefill kernel for GQA group " + std::to_string(group));
+    }
 #define HWKV_CASE(GG) \
     case GG:                                                                        \
         if (lay.dtype == HWKV_F16)                                                  \

@@ -178,13 +178,27 @@ def _unsupported_calls(lay, group):
     (48, 128, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (512, 64, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (16, 96, "bf16", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
-    (16, 256, "bf16", ["ok", "ok", "HWKV_ERR_UNSUPPORTED"]),
+    (16, 256, "bf16", ["ok", "ok", "ok"]),
+    (64, 256, "f16", ["ok", "ok", "ok"]),
     (16, 256, "f32", ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (16, 4, "bf16", ["HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
 ])
 def test_device_calls_without_a_kernel_are_rejected_before_launch(bs, d, dt, want):
     lay = hw.hwkv_layout_create([[64, 16]], bs, d, dt)
     got = _unsupported_calls(lay, 3)
+    for g, w in zip(got, want):
+        assert g == ("HWKV_ERR_INVALID_ARG" if w == "ok" else w)
+
+
+@pytest.mark.parametrize("d,group,want", [
+    (256, 4, ["ok", "ok", "ok"]),
+    (256, 6, ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+    (128, 8, ["ok", "ok", "ok"]),
+    (128, 5, ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+])
+def test_group_sizes_without_a_kernel_are_rejected_before_launch(d, group, want):
+    lay = hw.hwkv_layout_create([[64, 16]], 16, d, "bf16")
+    got = _unsupported_calls(lay, group)
     for g, w in zip(got, want):
         assert g == ("HWKV_ERR_INVALID_ARG" if w == "ok" else w)
 

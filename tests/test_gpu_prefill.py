@@ -187,3 +187,29 @@ def test_other_block_sizes_with_permuted_ids(bs, dtype):
     _check(to_host_f64(out), c.oracle())
     c16 = PrefillCase(windows, 128, 3, [9000, 130], 400, seed=712, dtype=dtype, block_size=16)
     assert torch.equal(out, c16.run())
+
+
+@pytest.mark.parametrize("G,dtype", [(1, torch.bfloat16), (2, torch.float16), (3, torch.bfloat16),
+                                     (4, torch.float16)])
+def test_head_dim_256(G, dtype):
+    """head_dim 256 (32 KiB K/V tiles, one wave per SIMD): ragged chunk end,
+    no history, windows shorter and longer than the chunk."""
+    say("prefill head_dim 256", G, dtype)
+    c = PrefillCase([33, 700, 4096, 1], 256, G, [1000, 40, 0], 150, seed=430 + G, dtype=dtype)
+    _check(to_host_f64(c.run()), c.oracle())
+
+
+def test_head_dim_256_block_sizes_bitwise():
+    """head_dim 256 with 64-token blocks and permuted ids equals 16-token
+    blocks bit for bit, and matches the oracle."""
+    windows = [2048, 300, 65]  # the longest a multiple of 64: both caches draw the same history
+    say("prefill head_dim 256 block size 64")
+    H = hw()
+    lay = H.hwkv_layout_create(np.array([windows], np.int32), 64, 256, torch.bfloat16)
+    bps = lay.desc().blocks_per_seq
+    perm = np.random.default_rng(64).permutation(2 * bps).astype(np.int32).reshape(2, bps)
+    c = PrefillCase(windows, 256, 2, [3000, 70], 200, seed=440, block_size=64, block_ids=perm)
+    out = c.run()
+    _check(to_host_f64(out), c.oracle())
+    c16 = PrefillCase(windows, 256, 2, [3000, 70], 200, seed=440, block_size=16)
+    assert torch.equal(out, c16.run())
