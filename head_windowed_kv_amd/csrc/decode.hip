@@ -782,7 +782,7 @@ bool decode_supported(const hwkv_layout& lay, int group) {
     if (bs < kBS || bs > 256 || (bs & (bs - 1)) != 0) return false;
     if (lay.dtype != HWKV_F32 && lay.dtype != HWKV_BF16 && lay.dtype != HWKV_F16) return false;
     if (lay.head_dim != 64 && lay.head_dim != 128 && lay.head_dim != 256) return false;
-    if (lay.head_dim == 256 && (lay.dtype == HWKV_F32 || group > 4)) return false;
+    if (lay.head_dim == 256 && lay.dtype == HWKV_F32) return false;
     switch (group) {
         case 1: case 2: case 3: case 4: case 6: case 8: return true;
         default: return false;
@@ -793,14 +793,15 @@ template <int MODE>
 hwkv_status launch_split_any(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                              hipStream_t s) {
     if (a.n_work_range <= 0) return HWKV_OK;
-    if (lay.head_dim == 256) {  // 16-bit caches, groups up to 4
+    if (lay.head_dim == 256) {  // 16-bit caches
         const bool f16 = lay.dtype == HWKV_F16;
 #define HWKV_CASE256(GG)                                                                     \
     case GG:                                                                                 \
         return f16 ? launch_split_t<kF16, 256, GG, MODE>(a, s)                               \
                    : launch_split_t<kBF16, 256, GG, MODE>(a, s);
         switch (group) {
-            HWKV_CASE256(1) HWKV_CASE256(2) HWKV_CASE256(3) HWKV_CASE256(4)
+            HWKV_CASE256(1) HWKV_CASE256(2) HWKV_CASE256(3) HWKV_CASE256(4) HWKV_CASE256(6)
+            HWKV_CASE256(8)
             default: break;
         }
 #undef HWKV_CASE256
@@ -849,6 +850,8 @@ hwkv_status launch_decode_merge(const hwkv_layout& lay, int group, const DecodeM
             case 2: return launch_merge_t<256, 2>(a, s);
             case 3: return launch_merge_t<256, 3>(a, s);
             case 4: return launch_merge_t<256, 4>(a, s);
+            case 6: return launch_merge_t<256, 6>(a, s);
+            case 8: return launch_merge_t<256, 8>(a, s);
             default: break;
         }
         return fail(HWKV_ERR_UNSUPPORTED, "no head_dim 256 merge kernel for GQA group " +

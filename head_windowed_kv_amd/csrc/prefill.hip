@@ -511,21 +511,20 @@ bool prefill_supported(const hwkv_layout& lay, int group) {
     if (lay.dtype != HWKV_BF16 && lay.dtype != HWKV_F16) return false;
     if (lay.head_dim != 64 && lay.head_dim != 128 && lay.head_dim != 256) return false;
     switch (group) {
-        case 1: case 2: case 3: case 4: return true;
-        case 6: case 8: return lay.head_dim != 256;
+        case 1: case 2: case 3: case 4: case 6: case 8: return true;
         default: return false;
     }
 }
 
 hwkv_status launch_prefill(const hwkv_layout& lay, int group, const PrefillArgs& a,
                            hipStream_t s) {
-    if (lay.head_dim == 256) {  // groups 1 to 4; one wave per SIMD (see the header)
+    if (lay.head_dim == 256) {  // one wave per SIMD (see the header)
 #define HWKV_CASE256(GG)                                                                     \
     case GG:                                                                                 \
         return lay.dtype == HWKV_F16 ? launch_t<kF16, 256, GG>(a, s)                         \
                                      : launch_t<kBF16, 256, GG>(a, s);
         switch (group) {
-            HWKV_CASE256(1) HWKV_CASE256(2) HWKV_CASE256(3) HWKV_CASE256(4)
+            HWKV_FOR_GROUPS(HWKV_CASE256)
             default: break;
         }
 #undef HWKV_CASE256

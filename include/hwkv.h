@@ -120,11 +120,10 @@ const char *hwkv_last_error(void);
  * head_dim in [1, 1024] and dtype F32, BF16 or F16 can be described and
  * estimated; the device calls report HWKV_ERR_UNSUPPORTED for combinations
  * that have no kernel (append: any block size, rows of whole 16-byte chunks;
- * decode: block sizes 16, 32, 64, 128, 256, head_dim 64 or 128 with F32,
- * BF16 or F16 and GQA groups 1, 2, 3, 4, 6, 8, head_dim 256 with BF16 or F16
- * and groups 1 to 4; prefill: the same block sizes, BF16 or F16, head_dim 64
- * or 128 with groups 1, 2, 3, 4, 6, 8 and head_dim 256 with groups 1 to
- * 4).  split_tokens is the decode split length S (a multiple of
+ * decode: block sizes 16, 32, 64, 128, 256, GQA groups 1, 2, 3, 4, 6, 8,
+ * head_dim 64 or 128 with F32, BF16 or F16 and head_dim 256 with BF16 or
+ * F16; prefill: the same block sizes and groups, BF16 or F16, head_dim 64,
+ * 128 or 256).  split_tokens is the decode split length S (a multiple of
  * block_size, at most max(block_size, 2048); 0 picks the largest multiple of
  * block_size not above 1024).  On success *out owns the layout; free it with
  * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1, a size

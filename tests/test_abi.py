@@ -192,7 +192,8 @@ def test_device_calls_without_a_kernel_are_rejected_before_launch(bs, d, dt, wan
 
 @pytest.mark.parametrize("d,group,want", [
     (256, 4, ["ok", "ok", "ok"]),
-    (256, 6, ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
+    (256, 6, ["ok", "ok", "ok"]),
+    (256, 5, ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
     (128, 8, ["ok", "ok", "ok"]),
     (128, 5, ["ok", "HWKV_ERR_UNSUPPORTED", "HWKV_ERR_UNSUPPORTED"]),
 ])

@@ -38,9 +38,9 @@ def test_f16_decode_instances(d, G):
 
 
 @pytest.mark.parametrize("dtype,G", [(torch.bfloat16, 1), (torch.bfloat16, 3), (torch.float16, 2),
-                                     (torch.float16, 4)])
+                                     (torch.float16, 4), (torch.bfloat16, 6), (torch.float16, 8)])
 def test_head_dim_256_decode(dtype, G):
-    """head_dim 256 (16-bit caches, GQA groups up to 4): one 16-byte chunk per
+    """head_dim 256 (16-bit caches, GQA groups 1 to 8): one 16-byte chunk per
     lane of 32-lane row groups."""
     windows = [[40, 700, 1, 2100], [16, 333, 1025, 64]]
     say("head_dim 256 decode", dtype, G)
@@ -49,25 +49,26 @@ def test_head_dim_256_decode(dtype, G):
     _check(c, run_decode_step(c))
 
 
-def test_head_dim_256_steps_bitwise():
+@pytest.mark.parametrize("G", [3, 8])
+def test_head_dim_256_steps_bitwise(G):
     """The appending entry points at head_dim 256 equal append + decode_attn."""
     H = hw()
     dev = device()
     windows = [[64, 1000, 17], [300, 16, 2048]]
     ctx = [2049, 16, 48]
     mk = dict(seed=707, split_tokens=512, chunk=300)
-    eager = build_decode_case(windows, torch.bfloat16, 256, 3, ctx, **mk)
-    two = build_decode_case(windows, torch.bfloat16, 256, 3, ctx, **mk)
-    one = build_decode_case(windows, torch.bfloat16, 256, 3, ctx, **mk)
-    say("head_dim 256 steps")
+    eager = build_decode_case(windows, torch.bfloat16, 256, G, ctx, **mk)
+    two = build_decode_case(windows, torch.bfloat16, 256, G, ctx, **mk)
+    one = build_decode_case(windows, torch.bfloat16, 256, G, ctx, **mk)
+    say("head_dim 256 steps", G)
     o_e = run_decode_step(eager)
     pos = torch.tensor([x - 1 for x in ctx], device=dev)
     o_t = torch.full_like(o_e, float("nan"))
     H.hwkv_decode_append_attn(two.cache, 0, 2, pos, two.k_new, two.v_new, two.q, 1 / 16.0,
-                              H.make_workspace(two.lay, 0, 2, 3, 9, device=dev), o_t)
+                              H.make_workspace(two.lay, 0, 2, 3, 3 * G, device=dev), o_t)
     o_o = torch.full_like(o_e, float("nan"))
     H.hwkv_decode_step(one.cache, 0, 2, pos, one.k_new, one.v_new, one.q, 1 / 16.0,
-                       H.make_step_workspace(one.lay, 0, 2, 3, 9, device=dev), o_o)
+                       H.make_step_workspace(one.lay, 0, 2, 3, 3 * G, device=dev), o_o)
     torch.cuda.synchronize()
     assert torch.equal(o_e, o_t) and torch.equal(o_e, o_o)
     assert torch.equal(eager.cache.pool, two.cache.pool)

@@ -190,7 +190,7 @@ def test_other_block_sizes_with_permuted_ids(bs, dtype):
 
 
 @pytest.mark.parametrize("G,dtype", [(1, torch.bfloat16), (2, torch.float16), (3, torch.bfloat16),
-                                     (4, torch.float16)])
+                                     (4, torch.float16), (6, torch.bfloat16), (8, torch.float16)])
 def test_head_dim_256(G, dtype):
     """head_dim 256 (32 KiB K/V tiles, one wave per SIMD): ragged chunk end,
     no history, windows shorter and longer than the chunk."""
