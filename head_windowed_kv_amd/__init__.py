@@ -375,8 +375,8 @@ def hwkv_decode_split(cache: Cache, layer_begin: int, n_layers: int, ctx_len: to
 def hwkv_decode_merge(cache: Cache, layer_begin: int, n_layers: int, ctx_len: torch.Tensor,
                       workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     d = cache.layout.desc()
-    if out.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("out must be float32 or bfloat16")
+    if out.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError("out must be float32, bfloat16 or float16")
     _expect("out", out, (n_layers, out.shape[1], out.shape[2], d.head_dim), out.dtype)
     _expect("ctx_len", ctx_len, (out.shape[1],), torch.int64)
     cv = cache.view()
@@ -392,8 +392,8 @@ def hwkv_decode_attn(cache: Cache, layer_begin: int, n_layers: int, ctx_len: tor
     """out: [n_layers][n_seqs][n_q_heads][head_dim] float32 or bfloat16."""
     d = cache.layout.desc()
     _expect("q", q, (n_layers, q.shape[1], q.shape[2], d.head_dim), torch_dtype(d.dtype))
-    if out.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("out must be float32 or bfloat16")
+    if out.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError("out must be float32, bfloat16 or float16")
     _expect("out", out, tuple(q.shape), out.dtype)
     _expect("ctx_len", ctx_len, (q.shape[1],), torch.int64)
     _expect_opt("seq_slots", seq_slots, (q.shape[1],), torch.int32)
@@ -416,8 +416,8 @@ def _decode_with_append(fn, cache: Cache, layer_begin: int, n_layers: int, pos: 
         kv_shape = (n_layers, n_seqs, 1, d.n_kv_heads, d.head_dim)
     _expect("k_new", k_new, kv_shape, torch_dtype(d.dtype))
     _expect("v_new", v_new, kv_shape, torch_dtype(d.dtype))
-    if out.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("out must be float32 or bfloat16")
+    if out.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError("out must be float32, bfloat16 or float16")
     _expect("out", out, tuple(q.shape), out.dtype)
     _expect("pos", pos, (n_seqs,), torch.int64)
     _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
@@ -482,8 +482,8 @@ def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Ten
     _expect("q", q, (n_seqs, n_chunk, n_q, d.head_dim), torch_dtype(d.dtype))
     _expect("k", k, (n_seqs, n_chunk, d.n_kv_heads, d.head_dim), torch_dtype(d.dtype))
     _expect("v", v, (n_seqs, n_chunk, d.n_kv_heads, d.head_dim), torch_dtype(d.dtype))
-    if out.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("out must be float32 or bfloat16")
+    if out.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError("out must be float32, bfloat16 or float16")
     _expect("out", out, tuple(q.shape), out.dtype)
     _expect("pos0", pos0, (n_seqs,), torch.int64)
     _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)

@@ -185,8 +185,8 @@ static hwkv_status merge_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     if (!ctx_len || !out) return fail(HWKV_ERR_INVALID_ARG, "null ctx_len or out");
     if (!aligned(ctx_len, 8)) return fail(HWKV_ERR_MISALIGNED, "ctx_len must be 8-byte aligned");
     if (!aligned(out, 16)) return fail(HWKV_ERR_MISALIGNED, "out must be 16-byte aligned");
-    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16)
-        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32 or HWKV_BF16");
+    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16 && out_dtype != HWKV_F16)
+        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32, HWKV_BF16 or HWKV_F16");
     *a = DecodeMergeArgs{};
     a->meta = static_cast<const uint8_t*>(c->meta);
     a->heads = reinterpret_cast<const HeadDesc*>(a->meta + L->heads_off);
@@ -203,7 +203,7 @@ static hwkv_status merge_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a->n_kv_heads = L->n_kv_heads;
     a->split_tokens = L->split_tokens;
     a->rec_floats = (int32_t)record_floats(*group, L->head_dim);
-    a->out_bf16 = out_dtype == HWKV_BF16;
+    a->out_kind = out_dtype;
     a->ctx_add = 0;
     return HWKV_OK;
 }
@@ -325,14 +325,14 @@ hwkv_status hwkv_decode_step(const hwkv_layout* L, const hwkv_cache* c, int32_t 
     if (!k_new || !v_new || !out) return fail(HWKV_ERR_INVALID_ARG, "null k_new, v_new or out");
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16))
         return fail(HWKV_ERR_MISALIGNED, "k_new, v_new and out must be 16-byte aligned");
-    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16)
-        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32 or HWKV_BF16");
+    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16 && out_dtype != HWKV_F16)
+        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32, HWKV_BF16 or HWKV_F16");
     a.k_new = static_cast<const uint8_t*>(k_new);
     a.v_new = static_cast<const uint8_t*>(v_new);
     a.pool_w = static_cast<uint8_t*>(c->pool);
     a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + (rec_bytes + 255) / 256 * 256);
     a.out = out;
-    a.out_bf16 = out_dtype == HWKV_BF16 ? 1 : 0;
+    a.out_kind = out_dtype;
     a.n_kv_heads = L->n_kv_heads;
     a.n_layers = n_layers;
     return launch_decode_step(*L, group, a, stream);
@@ -357,8 +357,8 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t
     if (!aligned(pos0, 8)) return fail(HWKV_ERR_MISALIGNED, "pos0 must be 8-byte aligned");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
         return fail(HWKV_ERR_MISALIGNED, "q, k, v and out must be 16-byte aligned");
-    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16)
-        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32 or HWKV_BF16");
+    if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16 && out_dtype != HWKV_F16)
+        return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32, HWKV_BF16 or HWKV_F16");
     if (!isfinite(scale)) return fail(HWKV_ERR_INVALID_ARG, "scale must be finite");
     PrefillArgs a{};
     a.pool = static_cast<const uint8_t*>(c->pool);
@@ -382,7 +382,7 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a.n_chunk = n_chunk;
     a.n_q_heads = n_q_heads;
     a.n_kv_heads = L->n_kv_heads;
-    a.out_bf16 = out_dtype == HWKV_BF16;
+    a.out_kind = out_dtype;
     a.tpb_log2 = 0;
     while ((16 << a.tpb_log2) < L->block_size) a.tpb_log2++;
     a.qk_scale_log2 = scale * 1.4426950408889634f;

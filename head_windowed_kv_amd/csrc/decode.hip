@@ -51,6 +51,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16
 typedef float f32x4 __attribute__((ext_vector_type(4)));     // 4 fp32
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -292,12 +293,17 @@ __device__ __forceinline__ float rec_get(const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Output row of (layer, sequence, kv head): G query heads x D, fp32 or bf16.
-__device__ __forceinline__ void store_out4(void* out, bool bf16, int64_t at, f32x4 o) {
-    if (bf16) {
+// Output row of (layer, sequence, kv head): G query heads x D, fp32, bf16 or fp16.
+__device__ __forceinline__ void store_out4(void* out, int kind, int64_t at, f32x4 o) {
+    if (kind == kBF16) {
         const uint32_t lo = (uint32_t)f32_to_bf16_rne(o.x) | ((uint32_t)f32_to_bf16_rne(o.y) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16_rne(o.z) | ((uint32_t)f32_to_bf16_rne(o.w) << 16);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + at) = make_uint2(lo, hi);
+    } else if (kind == kF16) {  // IEEE binary16, round to nearest even
+        const f16x2_t a = __builtin_convertvector(float2_t{o.x, o.y}, f16x2_t);
+        const f16x2_t b = __builtin_convertvector(float2_t{o.z, o.w}, f16x2_t);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + at) =
+            make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
     } else {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + at) = o;
     }
@@ -389,7 +395,7 @@ __device__ __forceinline__ float merge_den_part(const float* rec0, int rec_float
 // element.
 template <int D, int G, bool COH, int NTHREADS>
 __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0, int ds1, void* out,
-                             bool bf16, int64_t obase) {
+                             int out_kind, int64_t obase) {
     typedef MergeCfg<D, G> M;
     __shared__ f32x4 s_num[M::SG][M::NE4];
     __shared__ float s_den[M::SG][G];
@@ -426,7 +432,7 @@ __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0,
             tot.w = fmaf(f, x.w, tot.w);
             dtot = fmaf(f, s_den[k][h], dtot);
         }
-        store_out4(out, bf16, obase + c * 4,
+        store_out4(out, out_kind, obase + c * 4,
                    f32x4{tot.x / dtot, tot.y / dtot, tot.z / dtot, tot.w / dtot});
     }
 }
@@ -435,9 +441,9 @@ __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0,
 // split workgroup that finished last (records read with agent-coherent
 // loads): the same operations in the same order as decode_merge_kernel.
 template <int D, int G>
-__device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, void* out, bool bf16,
+__device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, void* out, int out_kind,
                                    int64_t obase) {
-    merge_chunks<D, G, true, kThreads>(rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, bf16,
+    merge_chunks<D, G, true, kThreads>(rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, out_kind,
                                        obase);
 }
 
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             const float x = __builtin_nanf("");
             for (int64_t e = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
                  e < n4; e += stride)
-                store_out4(a.out, a.out_bf16, e * 4, f32x4{x, x, x, x});
+                store_out4(a.out, a.out_kind, e * 4, f32x4{x, x, x, x});
         }
         return;
     }
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         if constexpr (FUSED) {  // no context: zeros, as the merge stage writes
             if (wk.split == 0)
                 for (int e = threadIdx.x; e < G * D / 4; e += kThreads)
-                    store_out4(a.out, a.out_bf16, obase + e * 4, f32x4{0.f, 0.f, 0.f, 0.f});
+                    store_out4(a.out, a.out_kind, obase + e * 4, f32x4{0.f, 0.f, 0.f, 0.f});
         }
         return;
     }
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             if (s_old != (uint32_t)(ns - 1)) return;
             const float* rec0 =
                 a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
-            merge_in_workgroup<D, G>(rec0, (int)ns, a.rec_floats, a.out, a.out_bf16, obase);
+            merge_in_workgroup<D, G>(rec0, (int)ns, a.rec_floats, a.out, a.out_kind, obase);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
@@ -732,7 +738,7 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
         const float x = fp != a.fingerprint ? __builtin_nanf("") : 0.f;
         for (int c = ds0 * M::CPS + (int)threadIdx.x; c < (ds0 + a.merge_chunks) * M::CPS;
              c += M::THREADS)
-            store_out4(a.out, a.out_bf16, obase + c * 4, f32x4{x, x, x, x});
+            store_out4(a.out, a.out_kind, obase + c * 4, f32x4{x, x, x, x});
         return;
     }
     const HeadDesc hd = a.heads[a.layer_begin * a.n_kv_heads + hrel];
@@ -741,7 +747,7 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     const float* rec0 =
         a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
     merge_chunks<D, G, false, M::THREADS>(rec0, ns, a.rec_floats, ds0, ds0 + a.merge_chunks, a.out,
-                                          a.out_bf16, obase);
+                                          a.out_kind, obase);
 }
 
 template <int T, int D, int G, int MODE>

@@ -157,7 +157,7 @@ struct DecodeSplitArgs {
     uint8_t* pool_w;
     uint32_t* counters;
     void* out;
-    int32_t out_bf16;
+    int32_t out_kind;  // element type of out (hwkv_dtype): F32, BF16 or F16
     int32_t n_kv_heads;
     int32_t n_layers;
 };
@@ -173,7 +173,7 @@ struct DecodeMergeArgs {
     int32_t layer_begin, n_layers, n_seqs, n_q_heads, n_kv_heads;
     int32_t split_tokens;
     int32_t rec_floats;
-    int32_t out_bf16;
+    int32_t out_kind;  // element type of out (hwkv_dtype): F32, BF16 or F16
     int32_t ctx_add;  // context = ctx_len[b] + ctx_add (1 when given positions)
     int32_t merge_chunks;  // column chunks per workgroup (set by the launcher)
 };
@@ -196,7 +196,7 @@ struct PrefillArgs {
     const uint8_t* v;
     void* out;
     int32_t layer, n_seqs, n_chunk, n_q_heads, n_kv_heads;
-    int32_t out_bf16;
+    int32_t out_kind;  // element type of out (hwkv_dtype): F32, BF16 or F16
     int32_t tpb_log2;  // log2(block_size / 16)
     float qk_scale_log2;
 };

@@ -475,9 +475,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             const int d0 = db * 32 + i * 8 + h2 * 4;
             const f32x4 o = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv,
                              oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv};
-            if (a.out_bf16) {
+            if (a.out_kind == kBF16) {
                 *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + obase + d0) =
                     u32x2{pack_bf16(o.x, o.y), pack_bf16(o.z, o.w)};
+            } else if (a.out_kind == kF16) {
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + obase + d0) =
+                    u32x2{pack_f16(o.x, o.y), pack_f16(o.z, o.w)};
             } else {
                 *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + d0) = o;
             }

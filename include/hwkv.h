@@ -216,8 +216,9 @@ hwkv_status hwkv_decode_split(const hwkv_layout *layout, const hwkv_cache *cache
 
 /* Decode attention, second stage: per (layer, sequence, query head) combine
  * the splits: M = max m_s, o = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
- * out: device [n_layers][n_seqs][n_q_heads][head_dim] as out_dtype.  A
- * sequence with ctx_len <= 0 gets zeros.  Same layer range, n_seqs, ctx_len
+ * out: device [n_layers][n_seqs][n_q_heads][head_dim] as out_dtype (F32, or
+ * BF16 / F16 rounded to nearest even from fp32).  A sequence with
+ * ctx_len <= 0 gets zeros.  Same layer range, n_seqs, ctx_len
  * and workspace as the split stage. */
 hwkv_status hwkv_decode_merge(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer_begin, int32_t n_layers,
@@ -300,7 +301,7 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * w-1 of them can be needed, and the ring holds at least w), keys from P on
  * from k, v.  q: device [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: device
  * [n_seqs][n_chunk][n_kv_heads][head_dim]; out: [n_seqs][n_chunk][n_q_heads]
- * [head_dim] as out_dtype.  The cache is read, not written: call hwkv_append
+ * [head_dim] as out_dtype (F32, BF16 or F16).  The cache is read, not written: call hwkv_append
  * with the same k, v (n_layers = 1) afterwards, since appending first could
  * overwrite history that earlier rows of the chunk still need.  Runs on
  * MFMA tiles (bf16 or fp16 operands, fp32 accumulation). */

@@ -68,6 +68,16 @@ def bf16_ulps_apart(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ia - ib)
 
 
+def f16_ulps_apart(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in binary16 units in the last place; each array is rounded
+    to binary16 first (numpy rounds to nearest even)."""
+    ia = a.astype(np.float16).view(np.int16).astype(np.int64)
+    ib = b.astype(np.float16).view(np.int16).astype(np.int64)
+    ia = np.where(ia < 0, -32768 - ia, ia)
+    ib = np.where(ib < 0, -32768 - ib, ib)
+    return np.abs(ia - ib)
+
+
 @dataclass
 class DecodeCase:
     """A cache filled by appending a logical token stream, plus one decode step.

@@ -13,7 +13,7 @@ import torch
 
 import synth
 from _gpu_common import (BF16_TOL, F32_TOL, bf16_round, bf16_ulps_apart, build_decode_case,
-                         build_stack_case, device, hw, oracle_decode, row_rel_err,
+                         build_stack_case, device, f16_ulps_apart, hw, oracle_decode, row_rel_err,
                          run_decode_step, say, stack_oracle_layer, stack_step, to_host_f64)
 
 pytestmark = pytest.mark.gpu
@@ -94,6 +94,17 @@ def test_bf16_output_within_one_ulp():
     out = run_decode_step(c, out_dtype=torch.bfloat16)
     ref = bf16_round(oracle_decode(c))
     ulps = bf16_ulps_apart(to_host_f64(out), ref)
+    assert ulps.max() <= 1, ulps.max()
+
+
+def test_f16_output_within_one_ulp():
+    """fp16 outputs (here from a bf16 cache): the fp32 result rounded to
+    nearest even, within one binary16 ulp of the oracle rounded the same way."""
+    windows = [[128, 1024, 4096, 33]]
+    say("f16 output")
+    c = build_decode_case(windows, torch.bfloat16, 128, 3, [5000, 70], seed=308)
+    out = run_decode_step(c, out_dtype=torch.float16)
+    ulps = f16_ulps_apart(out.cpu().numpy().astype(np.float64), oracle_decode(c))
     assert ulps.max() <= 1, ulps.max()
 
 

@@ -110,6 +110,19 @@ def test_bf16_output_and_scale():
     assert np.abs(got - ref_b).max() <= np.abs(ref).max() * 2 ** -7
 
 
+def test_f16_output():
+    """fp16 outputs: the oracle rounded to binary16 (nearest even), within half
+    a binary16 ulp of the largest output plus the kernel's own error (the
+    prefill's fp32 result carries ~1e-5 of the row maximum, so element-wise
+    ulps of small entries are not a fair measure)."""
+    say("prefill f16 out")
+    c = PrefillCase([64, 130, 2000], 128, 2, [500, 0], 100, seed=409)
+    got = c.run(out_dtype=torch.float16).cpu().numpy().astype(np.float64)
+    ref = c.oracle()
+    ref16 = ref.astype(np.float16).astype(np.float64)
+    assert np.abs(got - ref16).max() <= np.abs(ref).max() * 2 ** -10
+
+
 def test_chunk_size_invariance_and_last_row_equals_decode():
     """Prefill n rows at once == prefill n1, append n1, prefill the rest; the
     last row equals a decode step at L = P + n after appending the chunk."""

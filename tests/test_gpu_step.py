@@ -77,12 +77,13 @@ def test_step_equals_append_then_attn(case, two_launch):
     assert err <= (BF16_TOL if dtype == torch.bfloat16 else F32_TOL)
 
 
-def test_step_bf16_output_and_layer_subrange():
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_step_bf16_output_and_layer_subrange(out_dtype):
     windows = [[64, 128], [300, 16], [1000, 5], [77, 4000]]
-    say("fused step: bf16 output, layer subrange")
+    say("fused step: 16-bit output, layer subrange", out_dtype)
     eager, fused = _twins(windows, torch.bfloat16, 128, 3, [4500, 333], seed=611)
-    o_e = run_decode_step(eager, out_dtype=torch.bfloat16, layer_begin=1, n_layers=2, scale=0.05)
-    o_f = _fused(fused, out_dtype=torch.bfloat16, layer_begin=1, n_layers=2, scale=0.05)
+    o_e = run_decode_step(eager, out_dtype=out_dtype, layer_begin=1, n_layers=2, scale=0.05)
+    o_f = _fused(fused, out_dtype=out_dtype, layer_begin=1, n_layers=2, scale=0.05)
     assert torch.equal(o_e, o_f)
     assert torch.equal(eager.cache.pool, fused.cache.pool)
     # the two stage calls of the two-launch step: split (appending), merge
