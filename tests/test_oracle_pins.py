@@ -227,9 +227,10 @@ def test_decode_full_window_is_full_attention(dtype):
             assert np.abs(got[l, b] - ref.numpy()).max() <= 1e-12
 
 
+@pytest.mark.parametrize("d", [32, 256])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
-def test_decode_window_is_band_masked_attention(dtype):
-    n_layers, n_seqs, n_kv, G, d, T = 2, 3, 4, 2, 32, 200
+def test_decode_window_is_band_masked_attention(dtype, d):
+    n_layers, n_seqs, n_kv, G, T = 2, 3, 4, 2, 200
     q, k, v = _decode_case(dtype, n_layers, n_seqs, n_kv, G, d, T, 21)
     L = [200, 64, 129]
     windows = np.array([[1, 7, 64, 100], [33, 128, 2, 500]], np.int32)
@@ -466,9 +467,10 @@ def test_prefill_full_window_is_causal_attention(dtype):
         assert np.abs(got[b] - ref).max() <= 1e-12
 
 
+@pytest.mark.parametrize("d", [16, 256])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
-def test_prefill_window_is_band_masked_attention(dtype):
-    n_seqs, n_kv, G, d, P, n = 2, 3, 2, 16, 50, 40
+def test_prefill_window_is_band_masked_attention(dtype, d):
+    n_seqs, n_kv, G, P, n = 2, 3, 2, 50, 40
     q, kc, vc, kh, vh = _prefill_case(dtype, n_seqs, n_kv, G, d, P, n, 111)
     windows = [1, 17, 64]
     pos0 = [50, 0]
