@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <limits>
+#include <memory>
 #include <new>
 #include <string>
 
@@ -54,10 +55,28 @@ uint32_t hwkv_abi_version(void) { return HWKV_ABI_VERSION; }
 
 const char* hwkv_last_error(void) { return g_last_error.c_str(); }
 
+static hwkv_status layout_create(int32_t n_layers, int32_t n_kv_heads, const int32_t* windows,
+                                 int32_t block_size, int32_t head_dim, hwkv_dtype dtype,
+                                 int32_t split_tokens, hwkv_layout** out);
+
 hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32_t* windows,
                                int32_t block_size, int32_t head_dim, hwkv_dtype dtype,
                                int32_t split_tokens, hwkv_layout** out) {
     clear_error();
+    // the host tables can be large (a work list of up to 2^31 items): an
+    // allocation failure is reported, never thrown across the C ABI
+    try {
+        return layout_create(n_layers, n_kv_heads, windows, block_size, head_dim, dtype,
+                             split_tokens, out);
+    } catch (const std::bad_alloc&) {
+        if (out) *out = nullptr;
+        return fail(HWKV_ERR_INVALID_ARG, "out of host memory for the layout tables");
+    }
+}
+
+static hwkv_status layout_create(int32_t n_layers, int32_t n_kv_heads, const int32_t* windows,
+                                 int32_t block_size, int32_t head_dim, hwkv_dtype dtype,
+                                 int32_t split_tokens, hwkv_layout** out) {
     if (!out || !windows) return fail(HWKV_ERR_INVALID_ARG, "null windows or out pointer");
     *out = nullptr;
     if (n_layers < 1 || n_kv_heads < 1)
@@ -89,7 +108,7 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
                             std::to_string(i % n_kv_heads));
     }
 
-    hwkv_layout* L = new (std::nothrow) hwkv_layout();
+    std::unique_ptr<hwkv_layout> L(new (std::nothrow) hwkv_layout());
     if (!L) return fail(HWKV_ERR_INVALID_ARG, "out of host memory");
     L->n_layers = n_layers;
     L->n_kv_heads = n_kv_heads;
@@ -124,10 +143,8 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
         acc += nb;
         work += ns;
         if (w > maxw) maxw = (int32_t)w;
-        if (work > std::numeric_limits<int32_t>::max() || acc > std::numeric_limits<int32_t>::max()) {
-            delete L;
+        if (work > std::numeric_limits<int32_t>::max() || acc > std::numeric_limits<int32_t>::max())
             return fail(HWKV_ERR_OVERFLOW, "decode work list or blocks per sequence exceed int32");
-        }
     }
     L->head_off[n_heads] = acc;
     L->layer_work_off[n_layers] = (int32_t)work;
@@ -167,7 +184,7 @@ hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads, const int32
     off = align_up(off + (uint64_t)n_heads * sizeof(int32_t), kMetaAlign);
     L->meta_bytes = off;
 
-    *out = L;
+    *out = L.release();
     return HWKV_OK;
 }
 
