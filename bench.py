@@ -491,18 +491,23 @@ def prefill_leg(H, torch, synth):
     pos = torch.full((n_seqs,), P, dtype=torch.int64, device=dev)
     scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream()
-    for _ in range(2):
-        H.hwkv_prefill_attn(cache, 0, pos, q, k, v, out, scale)
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(10):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        H.hwkv_prefill_attn(cache, 0, pos, q, k, v, out, scale)
-        e1.record(s)
+
+    def median_ms(fn, reps=10):
+        for _ in range(2):
+            fn(cache, 0, pos, q, k, v, out, scale)
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    pf_ms = sorted(ts)[len(ts) // 2]
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn(cache, 0, pos, q, k, v, out, scale)
+            e1.record(s)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+    # P in fp16 (the default entry) and P split into two bf16 products
+    exact_ms = median_ms(H.hwkv_prefill_attn_exact, 5)
+    pf_ms = median_ms(H.hwkv_prefill_attn)
     # algorithmic flops: per query row and query head, 4 d flops per key in
     # its window [p-w+1, p] (QK^T and PV, 2 flops per multiply-add)
     keys = 0
@@ -555,6 +560,9 @@ def prefill_leg(H, torch, synth):
             "gemm_reference_tflops": round(gemm_tf, 1),
             "frac_of_gemm_reference": round(flop / (pf_ms / 1e3) / 1e12 / gemm_tf, 4),
             "prefill_tokens_per_s": round(n_seqs * n / (pf_ms / 1e3), 1),
+            "p_in_pv_product": "fp16 (V converted to fp16 on chip; exact re-run if out of range)",
+            "prefill_exact_ms": round(exact_ms, 4),
+            "prefill_exact_tflops": round(flop / (exact_ms / 1e3) / 1e12, 1),
             "chunk_append_ms": round(append_ms, 4),
             "decode_step_ms": round(dec_ms, 4),
             "decode_tokens_per_s": round(n_seqs / (dec_ms / 1e3), 1),

@@ -43,7 +43,7 @@ EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_l
             "hwkv_decode_attn", "hwkv_decode_split_append", "hwkv_decode_append_attn",
             "hwkv_step_workspace_bytes",
             "hwkv_decode_step",
-            "hwkv_prefill_attn")
+            "hwkv_prefill_attn", "hwkv_prefill_attn_exact")
 
 
 class hwkv_layout_desc(ctypes.Structure):
@@ -109,9 +109,10 @@ _lib.hwkv_step_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _i32, _P(_u64)
 _lib.hwkv_decode_step.restype = ctypes.c_int
 _lib.hwkv_decode_step.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                   _i32, _vp, _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
-_lib.hwkv_prefill_attn.restype = ctypes.c_int
-_lib.hwkv_prefill_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _vp, _vp, _i32, _i32, _vp,
-                                   _vp, _vp, _vp, ctypes.c_int, _f32, _vp]
+for _name in ("hwkv_prefill_attn", "hwkv_prefill_attn_exact"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _vp, _vp, _i32, _i32, _vp,
+                                     _vp, _vp, _vp, ctypes.c_int, _f32, _vp]
 
 
 class HwkvError(RuntimeError):
@@ -476,7 +477,20 @@ def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.T
 def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,
                       k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, scale: float,
                       seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
-    """q, out: [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: [n_seqs][n_chunk][n_kv][head_dim]."""
+    """q, out: [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: [n_seqs][n_chunk][n_kv][head_dim].
+    P enters the P.V product in fp16."""
+    _prefill(_lib.hwkv_prefill_attn, cache, layer, pos0, q, k, v, out, scale, seq_slots, stream)
+
+
+def hwkv_prefill_attn_exact(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,
+                            k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, scale: float,
+                            seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """hwkv_prefill_attn with P split into two bf16 products for bf16 caches."""
+    _prefill(_lib.hwkv_prefill_attn_exact, cache, layer, pos0, q, k, v, out, scale, seq_slots,
+             stream)
+
+
+def _prefill(fn, cache, layer, pos0, q, k, v, out, scale, seq_slots, stream) -> None:
     d = cache.layout.desc()
     n_seqs, n_chunk, n_q = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     _expect("q", q, (n_seqs, n_chunk, n_q, d.head_dim), torch_dtype(d.dtype))
@@ -488,10 +502,9 @@ def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Ten
     _expect("pos0", pos0, (n_seqs,), torch.int64)
     _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
     cv = cache.view()
-    _check(_lib.hwkv_prefill_attn(cache.layout.handle, ctypes.byref(cv), layer, int(q.shape[0]),
-                                  _ptr(seq_slots), _ptr(pos0), int(q.shape[1]), int(q.shape[2]),
-                                  _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(out.dtype),
-                                  scale, _stream(stream)))
+    _check(fn(cache.layout.handle, ctypes.byref(cv), layer, int(q.shape[0]), _ptr(seq_slots),
+              _ptr(pos0), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+              _dtype_code(out.dtype), scale, _stream(stream)))
 
 
 def loaded_library_path() -> str:

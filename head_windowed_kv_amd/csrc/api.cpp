@@ -338,11 +338,11 @@ hwkv_status hwkv_decode_step(const hwkv_layout* L, const hwkv_cache* c, int32_t 
     return launch_decode_step(*L, group, a, stream);
 }
 
-hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
-                              int32_t n_seqs, const int32_t* seq_slots, const int64_t* pos0,
-                              int32_t n_chunk, int32_t n_q_heads, const void* q, const void* k,
-                              const void* v, void* out, hwkv_dtype out_dtype, float scale,
-                              hipStream_t stream) {
+static hwkv_status prefill_entry(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
+                                 int32_t n_seqs, const int32_t* seq_slots, const int64_t* pos0,
+                                 int32_t n_chunk, int32_t n_q_heads, const void* q,
+                                 const void* k, const void* v, void* out, hwkv_dtype out_dtype,
+                                 float scale, bool exact_p, hipStream_t stream) {
     clear_error();
     HWKV_TRY(check_cache(L, c));
     HWKV_TRY(check_batch(L, c, layer, 1, n_seqs, seq_slots));
@@ -385,8 +385,27 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t
     a.out_kind = out_dtype;
     a.tpb_log2 = 0;
     while ((16 << a.tpb_log2) < L->block_size) a.tpb_log2++;
+    a.exact_p = exact_p ? 1 : 0;
     a.qk_scale_log2 = scale * 1.4426950408889634f;
     return launch_prefill(*L, group, a, stream);
+}
+
+hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
+                              int32_t n_seqs, const int32_t* seq_slots, const int64_t* pos0,
+                              int32_t n_chunk, int32_t n_q_heads, const void* q, const void* k,
+                              const void* v, void* out, hwkv_dtype out_dtype, float scale,
+                              hipStream_t stream) {
+    return prefill_entry(L, c, layer, n_seqs, seq_slots, pos0, n_chunk, n_q_heads, q, k, v, out,
+                         out_dtype, scale, false, stream);
+}
+
+hwkv_status hwkv_prefill_attn_exact(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
+                                    int32_t n_seqs, const int32_t* seq_slots,
+                                    const int64_t* pos0, int32_t n_chunk, int32_t n_q_heads,
+                                    const void* q, const void* k, const void* v, void* out,
+                                    hwkv_dtype out_dtype, float scale, hipStream_t stream) {
+    return prefill_entry(L, c, layer, n_seqs, seq_slots, pos0, n_chunk, n_q_heads, q, k, v, out,
+                         out_dtype, scale, true, stream);
 }
 
 }  // extern "C"

@@ -198,6 +198,7 @@ struct PrefillArgs {
     int32_t layer, n_seqs, n_chunk, n_q_heads, n_kv_heads;
     int32_t out_kind;  // element type of out (hwkv_dtype): F32, BF16 or F16
     int32_t tpb_log2;  // log2(block_size / 16)
+    int32_t exact_p;   // bf16 caches: P split into two bf16 products, no fp16 pass
     float qk_scale_log2;
 };
 

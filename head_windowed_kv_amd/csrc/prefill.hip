@@ -18,10 +18,15 @@
 //                 LDS read), B = P^T taken straight from the S^T registers; the
 //                 key order of the two operands is matched through the
 //                 transpose-read addresses.
-// bf16 caches: P is split into a bf16 high part and a bf16 remainder (two
-// MFMAs), since P rounded to bf16 alone costs ~2e-3 relative error on
-// near-uniform softmax rows.  fp16 caches use v_mfma_f32_32x32x16_f16 and one
-// PV product: P rounded to fp16 (11 significant bits) is 8x more accurate.
+// P rounded to bf16 alone costs ~3e-3 relative error on near-uniform softmax
+// rows, so the PV product takes P in fp16 (11 significant bits, 8x more
+// accurate) on v_mfma_f32_32x32x16_f16.  fp16 caches hold V in fp16 already;
+// for bf16 caches each wave converts its own slice of every V tile in LDS
+// after the slice's DMA lands (exact for |v| in fp16's normal range), and a
+// workgroup whose result shows a value outside that range (a non-finite or
+// a very small output row) runs again on the stored bf16 tiles with P split
+// into a bf16 high part and a bf16 remainder (two MFMAs).  That exact form is
+// also what hwkv_prefill_attn_exact runs directly.
 //
 // head_dim 256: the accumulators and query operands take twice the registers
 // (484 VGPRs), so that instance runs one wave per SIMD, with 32 KiB tiles.
@@ -91,6 +96,18 @@ __device__ __forceinline__ int swz_v(int r) {
     return D >= 128 ? 2 * ((2 * (r & 3)) ^ ((r >> 1) & 1)) : 2 * (r & 3);
 }
 
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations and leaves the other counters alone
+template <int n>
+constexpr int vmcnt_imm() {
+    return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float xor32f(float x) { return __shfl_xor(x, 32, 64); }
@@ -141,8 +158,9 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, ui
 }
 
 // BIG: cache blocks of more than 16 tokens (the 16-token case keeps every
-// slice address a compile-time constant)
-template <int KT, int D, int G, bool BIG>
+// slice address a compile-time constant).  EXACT (bf16 caches): only the pass
+// with P split into two bf16 products.
+template <int KT, int D, int G, bool BIG, bool EXACT>
 __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(PrefillArgs a) {
     typedef PfCfg<D> C;
     // two stages of K and V tiles; separate objects so that the compiler sees
@@ -151,6 +169,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TILE];
+    __shared__ int s_redo;  // a workgroup's fp16 pass must be redone exactly
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,6 +193,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
     if (fp != a.fingerprint) return;
+    if (threadIdx.x == 0) s_redo = 0;  // read only after later barriers
     const int rank = pair / a.n_seqs;
     const int b = pair % a.n_seqs;
     const int kvh = a.order[(int64_t)a.layer * a.n_kv_heads + rank];
@@ -344,16 +364,17 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     };
 
     f32x16 oacc[C::DBLK];
-#pragma unroll
-    for (int db = 0; db < C::DBLK; db++) oacc[db] = f32x16{};
     // running max in the log2 domain; it is only raised when some lane's tile
     // maximum exceeds it by more than kLazy, so P stays below 2^kLazy
     float m_run = kEmptyMax, l_run = 0.f;
 
-    // P = 2^(s c2 - m) of k-step ks (keys 16 ks .. 16 ks + 15) as B operands:
-    // high part = P truncated to bf16, low part = the exact remainder rounded
-    // to bf16; psum collects the fp32 P values
-    auto make_p = [&](const f32x16* sc, int ks, u32x4& hi, u32x4& lo, float& psum) {
+    // P = 2^(s c2 - m) of k-step ks (keys 16 ks .. 16 ks + 15) as B operands.
+    // F16P: P rounded to fp16, one operand.  Otherwise high part = P
+    // truncated to bf16, low part = the exact remainder rounded to bf16.
+    // psum collects the fp32 P values.
+    auto make_p = [&](auto f16p_tag, const f32x16* sc, int ks, u32x4& hi, u32x4& lo,
+                      float& psum) {
+        constexpr bool F16P = decltype(f16p_tag)::value;
         const int kb2 = ks >> 1, half = ks & 1;
         uint32_t hw[4], lw[4];
         float ps[4];
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             const float pa = fast_exp2(fmaf(sc[kb2][r0], c2, -m_run));
             const float pb2 = fast_exp2(fmaf(sc[kb2][r0 + 1], c2, -m_run));
             const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb2);
-            if constexpr (KT == kF16) {
+            if constexpr (F16P) {
                 hw[e] = pack_f16(pa, pb2);
                 lw[e] = 0;
             } else {
@@ -379,7 +400,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     };
 
     // O^T += V^T P^T for k-step ks; the V^T operands come from transpose reads
-    auto pv = [&](const uint8_t* vt, int ks, const u32x4& hi, const u32x4& lo) {
+    // (fp16 when F16P: an fp16 cache, or a bf16 tile converted in LDS)
+    auto pv = [&](auto f16p_tag, const uint8_t* vt, int ks, const u32x4& hi, const u32x4& lo) {
+        constexpr bool F16P = decltype(f16p_tag)::value;
         const int roff = ((ks >> 1) * 32 + (ks & 1) * 16) * C::ROW;
         u32x4 va[C::DBLK];
 #pragma unroll
@@ -388,78 +411,172 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             const u32x2 r1 = tr_read(vt + roff + 8 * C::ROW + vaddr[db]);
             va[db] = u32x4{r0.x, r0.y, r1.x, r1.y};
         }
+        if constexpr (F16P) {
 #pragma unroll
-        for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<KT>(va[db], hi, oacc[db]);
-        if constexpr (KT == kBF16) {
+            for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<kF16>(va[db], hi, oacc[db]);
+        } else {
+#pragma unroll
+            for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<KT>(va[db], hi, oacc[db]);
 #pragma unroll
             for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<KT>(va[db], lo, oacc[db]);
         }
     };
 
+    // bf16 -> fp16 in place over this wave's 16-key slice of a V tile (the
+    // slice its own DMA filled).  Exact while |v| lies in fp16's normal
+    // range; values outside it are caught by the check after the key loop.
+    auto slice_to_f16 = [&](uint8_t* vbuf) {
+        uint8_t* base = vbuf + wave * (kBS * C::ROW) + lane * 16;
+        u32x4 x[C::NI];
+#pragma unroll
+        for (int j = 0; j < C::NI; j++) x[j] = *reinterpret_cast<const u32x4*>(base + j * 1024);
+#pragma unroll
+        for (int j = 0; j < C::NI; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t w2 = x[j][e];
+                x[j][e] = pack_f16(__uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u));
+            }
+#pragma unroll
+        for (int j = 0; j < C::NI; j++) *reinterpret_cast<u32x4*>(base + j * 1024) = x[j];
+    };
+
     // ---- software pipeline over key tiles ----
     // Iteration it (tile T = T0 + it) finds S^T of T in registers and K of
-    // T + 1, V of T in LDS; it starts the DMA of K of T + 2 and V of T + 1,
+    // T + 1, V of T in LDS; it starts the DMA of V of T + 1 and K of T + 2,
     // computes S^T of T + 1 while it exponentiates T, and multiplies P of T
-    // into O while it finishes the exponentials and masks T + 1.
+    // into O while it finishes the exponentials and masks T + 1.  When V is
+    // converted to fp16, each wave converts its slice of V of T + 1 at the
+    // end of the iteration (waiting for its own DMA of it only); the next
+    // iteration's barrier publishes the slice to the other waves.
     f32x16 sA[2], sB[2];  // S^T of the current and of the next tile, alternating
     float mt = kEmptyMax;
     int32_t idK = 0, idV = 0;
-    if (n_tiles > 0) {
-        const int32_t id0 = next_id();
-        issue(sK0, T0, id0, false);
-        issue(sV0, T0, id0, true);
-        const int32_t id1 = next_id();
-        if (n_tiles > 1) issue(sK1, T0 + 1, id1, false);
-        idV = id1;
-        idK = next_id();
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (wave_on && n_tiles > 0) {
-        qk(sK0, sA[0], sA[1]);
-        mt = mask_max(sA, T0);
-    }
-
-    auto step = [&](int it, const uint8_t* k_rd, const uint8_t* v_rd, uint8_t* k_dma, uint8_t* v_dma,
-                    f32x16* s_cur, f32x16* s_next) {
-        const int64_t T = T0 + it;
-        // K of T + 1 and V of T have landed (the wait covers this wave's LDS
-        // DMA, which the compiler does not track); K of T, V of T - 1 are free
+    auto run = [&](auto f16p_tag) {
+        constexpr bool F16P = decltype(f16p_tag)::value;
+        constexpr bool CONV = F16P && KT == kBF16;
+        u_next = (uint32_t)(T0 * (kBK / kBS) + wave);
+        jw = (int32_t)((u_next >> tpb_log2) % (uint32_t)nb);
+        m_run = kEmptyMax;
+        l_run = 0.f;
+        mt = kEmptyMax;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; db++) oacc[db] = f32x16{};
+        if (n_tiles > 0) {
+            const int32_t id0 = next_id();
+            issue(sK0, T0, id0, false);
+            issue(sV0, T0, id0, true);
+            const int32_t id1 = next_id();
+            if (n_tiles > 1) issue(sK1, T0 + 1, id1, false);
+            idV = id1;
+            idK = next_id();
+        }
         __builtin_amdgcn_s_waitcnt(0);
+        if (CONV && n_tiles > 0) {
+            __asm__ volatile("" ::: "memory");
+            slice_to_f16(sV0);
+        }
         __syncthreads();
-        if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
-        if (it + 1 < n_tiles) issue(v_dma, T + 1, idV, true);
-        idV = idK;
-        idK = next_id();
-        if (!wave_on) return;
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+        if (wave_on && n_tiles > 0) {
+            qk(sK0, sA[0], sA[1]);
+            mt = mask_max(sA, T0);
+        }
+
+        // this wave's DMA of V of T + 1 has landed (the K DMA issued after
+        // it may still be in flight)
+        auto convert_next_v = [&](int it, uint8_t* v_dma) {
+            if (it + 2 < n_tiles)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm<C::NI>());
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+            __asm__ volatile("" ::: "memory");
+            slice_to_f16(v_dma);
+        };
+        auto step = [&](int it, const uint8_t* k_rd, const uint8_t* v_rd, uint8_t* k_dma,
+                        uint8_t* v_dma, f32x16* s_cur, f32x16* s_next) {
+            const int64_t T = T0 + it;
+            // K of T + 1 and V of T have landed (the wait covers this wave's
+            // LDS DMA, which the compiler does not track); K of T, V of T - 1
+            // are free
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if constexpr (CONV) {  // V first: its wait below leaves the K DMA in flight
+                if (it + 1 < n_tiles) issue(v_dma, T + 1, idV, true);
+                if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
+            } else {
+                if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
+                if (it + 1 < n_tiles) issue(v_dma, T + 1, idV, true);
+            }
+            idV = idK;
+            idK = next_id();
+            if (!wave_on) {
+                if (CONV && it + 1 < n_tiles) convert_next_v(it, v_dma);
+                return;
+            }
+            if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::DBLK; db++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) oacc[db][r] *= alpha;
+            }
+            u32x4 phi[4], plo[4];
+            float psum = 0.f;
+            qk(k_rd, s_next[0], s_next[1]);
+            make_p(f16p_tag, s_cur, 0, phi[0], plo[0], psum);
+            make_p(f16p_tag, s_cur, 1, phi[1], plo[1], psum);
+            pv(f16p_tag, v_rd, 0, phi[0], plo[0]);
+            pv(f16p_tag, v_rd, 1, phi[1], plo[1]);
+            make_p(f16p_tag, s_cur, 2, phi[2], plo[2], psum);
+            make_p(f16p_tag, s_cur, 3, phi[3], plo[3], psum);
+            pv(f16p_tag, v_rd, 2, phi[2], plo[2]);
+            pv(f16p_tag, v_rd, 3, phi[3], plo[3]);
+            l_run += psum;
+            if (it + 1 < n_tiles) mt = mask_max(s_next, T + 1);
+            if (CONV && it + 1 < n_tiles) convert_next_v(it, v_dma);
+        };
+        for (int it = 0; it < n_tiles; it += 2) {
+            step(it, sK1, sV0, sK0, sV1, sA, sB);
+            if (it + 1 >= n_tiles) break;
+            step(it + 1, sK0, sV1, sK1, sV0, sB, sA);
+        }
+    };
+
+    if constexpr (KT == kBF16 && EXACT) {
+        run(BoolC<false>{});
+    } else if constexpr (KT == kBF16) {
+        // First pass with P and V in fp16 (one PV product).  The conversion
+        // of V is exact for |v| in [2^-14, 65504]; a larger value becomes inf
+        // and poisons its output column (inf or NaN), and smaller values lose
+        // at most 2^-25 each.  A workgroup in which some live row came out
+        // non-finite, or with a maximum below 2^-12 (where that absolute error
+        // could matter), runs again with P split into two bf16 products and
+        // the bf16 V tiles as stored.
+        run(BoolC<true>{});
+        if (wave_on) {
+            float sa = 0.f, mx = 0.f;
 #pragma unroll
             for (int db = 0; db < C::DBLK; db++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) oacc[db][r] *= alpha;
+                for (int i = 0; i < 16; i++) {
+                    const float x = fabsf(oacc[db][i]);
+                    sa += x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, xor32f(mx));
+            const float l_tot = l_run + xor32f(l_run);
+            const bool ok = __builtin_isfinite(sa) && __builtin_isfinite(l_tot) &&
+                            mx >= 0x1p-12f * l_tot;
+            const bool live = p0 - P + col < n && seq_ok;
+            if (__builtin_amdgcn_ballot_w64(live && !ok) != 0 && lane == 0) s_redo = 1;
         }
-        u32x4 phi[4], plo[4];
-        float psum = 0.f;
-        qk(k_rd, s_next[0], s_next[1]);
-        make_p(s_cur, 0, phi[0], plo[0], psum);
-        make_p(s_cur, 1, phi[1], plo[1], psum);
-        pv(v_rd, 0, phi[0], plo[0]);
-        pv(v_rd, 1, phi[1], plo[1]);
-        make_p(s_cur, 2, phi[2], plo[2], psum);
-        make_p(s_cur, 3, phi[3], plo[3], psum);
-        pv(v_rd, 2, phi[2], plo[2]);
-        pv(v_rd, 3, phi[3], plo[3]);
-        l_run += psum;
-        if (it + 1 < n_tiles) mt = mask_max(s_next, T + 1);
-    };
-    for (int it = 0; it < n_tiles; it += 2) {
-        step(it, sK1, sV0, sK0, sV1, sA, sB);
-        if (it + 1 >= n_tiles) break;
-        step(it + 1, sK0, sV1, sK1, sV0, sB, sA);
+        __syncthreads();
+        if (s_redo) run(BoolC<false>{});
+    } else {
+        run(BoolC<true>{});
     }
 
     // ---- normalise and write this lane's query row ----
@@ -489,7 +606,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
 
 template <int T, int D, int G>
 hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
-    auto kernel = a.tpb_log2 > 0 ? prefill_kernel<T, D, G, true> : prefill_kernel<T, D, G, false>;
+    auto kernel = a.tpb_log2 > 0 ? prefill_kernel<T, D, G, true, false>
+                                 : prefill_kernel<T, D, G, false, false>;
+    if constexpr (T == kBF16) {
+        if (a.exact_p)
+            kernel = a.tpb_log2 > 0 ? prefill_kernel<T, D, G, true, true>
+                                    : prefill_kernel<T, D, G, false, true>;
+    }
     const int n_pb = (a.n_chunk + kQW - 1) / kQW;
     const int n_units = G * n_pb;
     const int64_t n_groups = (n_units + kWaves - 1) / kWaves;

@@ -304,7 +304,17 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * [head_dim] as out_dtype (F32, BF16 or F16).  The cache is read, not written: call hwkv_append
  * with the same k, v (n_layers = 1) afterwards, since appending first could
  * overwrite history that earlier rows of the chunk still need.  Runs on
- * MFMA tiles (bf16 or fp16 operands, fp32 accumulation). */
+ * MFMA tiles (bf16 or fp16 operands, fp32 accumulation).
+ *
+ * Precision of the softmax weights P in the P.V product: they are rounded
+ * once to fp16 (11 significant bits; row error a few 1e-4 of the row's
+ * largest output on N(0,1) data).  For BF16 caches this needs V in fp16:
+ * each V tile is converted in on-chip memory, which is exact for |v| in
+ * [2^-14, 65504].  A workgroup with a non-finite output (a V element
+ * beyond fp16's range) or with a row whose largest output magnitude is below
+ * 2^-12 (where the conversion's absolute error, at most 2^-25 per element,
+ * could matter) is recomputed as hwkv_prefill_attn_exact does, so such
+ * inputs cost time, not accuracy. */
 hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer, int32_t n_seqs,
                               const int32_t *seq_slots, const int64_t *pos0,
@@ -312,6 +322,20 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache
                               const void *k, const void *v, void *out,
                               hwkv_dtype out_dtype, float scale,
                               hipStream_t stream);
+
+/* hwkv_prefill_attn with the P.V product at ~16-bit precision for BF16
+ * caches: P is split into its truncation to bf16 and the remainder rounded
+ * to bf16, two bf16 products (row error ~1e-5 of the row's largest output),
+ * at about 10% more time.  For F16 caches it is hwkv_prefill_attn.  Same
+ * arguments, layouts and errors. */
+hwkv_status hwkv_prefill_attn_exact(const hwkv_layout *layout,
+                                    const hwkv_cache *cache, int32_t layer,
+                                    int32_t n_seqs, const int32_t *seq_slots,
+                                    const int64_t *pos0, int32_t n_chunk,
+                                    int32_t n_q_heads, const void *q,
+                                    const void *k, const void *v, void *out,
+                                    hwkv_dtype out_dtype, float scale,
+                                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -168,6 +168,9 @@ def _unsupported_calls(lay, group):
                                       p[4], 0, None)
     st_pf = hw._lib.hwkv_prefill_attn(lay.handle, ctypes.byref(cv), 0, 1, None, p[0], 0, n_q,
                                       p[3], p[1], p[2], p[4], 0, 0.1, None)
+    st_pfx = hw._lib.hwkv_prefill_attn_exact(lay.handle, ctypes.byref(cv), 0, 1, None, p[0], 0,
+                                             n_q, p[3], p[1], p[2], p[4], 0, 0.1, None)
+    assert st_pfx == st_pf  # the exact variant validates the same way
     return [hw.STATUS_NAMES[x] for x in (st_app, st_dec, st_pf)]
 
 
