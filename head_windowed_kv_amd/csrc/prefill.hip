@@ -110,7 +110,19 @@ constexpr int vmcnt_imm() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32f(float x) { return __shfl_xor(x, 32, 64); }
+// this lane's value and that of lane l ^ 32, in the two halves of one
+// v_permlane32_swap (each lane gets the pair in the same order as its partner)
+__device__ __forceinline__ f32x2 with_partner(float x) {
+    const u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    return f32x2{__uint_as_float(r.x), __uint_as_float(r.y)};
+}
+
+// NaN-propagating maximum: maps to v_maximum3_f32 chains with no operand
+// canonicalisation (fmaxf would first quiet every operand)
+__device__ __forceinline__ float fmaximum(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -353,14 +365,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
                     if (!((uint32_t)uu < (uint32_t)w)) sc[kb2][r] = -INFINITY;
                 }
         }
-        float m8[8];
+        float m0 = sc[0][0], m1 = sc[1][0];
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            m8[i] = fmaxf(fmaxf(sc[i >> 2][4 * (i & 3)], sc[i >> 2][4 * (i & 3) + 1]),
-                          fmaxf(sc[i >> 2][4 * (i & 3) + 2], sc[i >> 2][4 * (i & 3) + 3]));
-        const float mt = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                               fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-        return fmaxf(mt, xor32f(mt)) * c2;
+        for (int r = 1; r < 16; r++) {
+            m0 = fmaximum(m0, sc[0][r]);
+            m1 = fmaximum(m1, sc[1][r]);
+        }
+        const f32x2 pr = with_partner(fmaximum(m0, m1));
+        return fmaximum(pr.x, pr.y) * c2;
     };
 
     f32x16 oacc[C::DBLK];
@@ -369,9 +381,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     float m_run = kEmptyMax, l_run = 0.f;
 
     // P = 2^(s c2 - m) of k-step ks (keys 16 ks .. 16 ks + 15) as B operands.
-    // F16P: P rounded to fp16, one operand.  Otherwise high part = P
-    // truncated to bf16, low part = the exact remainder rounded to bf16.
-    // psum collects the fp32 P values.
+    // F16P: P rounded to fp16, one operand; psum collects the rounded values,
+    // so that numerator and denominator use the same weights.  Otherwise high
+    // part = P truncated to bf16, low part = the exact remainder rounded to
+    // bf16, and psum collects the fp32 P values.
     auto make_p = [&](auto f16p_tag, const f32x16* sc, int ks, u32x4& hi, u32x4& lo,
                       float& psum) {
         constexpr bool F16P = decltype(f16p_tag)::value;
@@ -391,12 +404,23 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
                 hw[e] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
                 lw[e] = pack_bf16(pa - __uint_as_float(ua & 0xffff0000u),
                                   pb2 - __uint_as_float(ub & 0xffff0000u));
+                ps[e] = pa + pb2;
             }
-            ps[e] = pa + pb2;
         }
         hi = u32x4{hw[0], hw[1], hw[2], hw[3]};
         lo = u32x4{lw[0], lw[1], lw[2], lw[3]};
-        psum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        if constexpr (F16P) {
+            // the row sum of the fp16 weights the P.V product uses, in fp32
+            // (v_dot2_f32_f16 against (1, 1))
+            const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            float q0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[0]), one2, 0.f, false);
+            float q1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[2]), one2, 0.f, false);
+            q0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[1]), one2, q0, false);
+            q1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[3]), one2, q1, false);
+            psum += q0 + q1;
+        } else {
+            psum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        }
     };
 
     // O^T += V^T P^T for k-step ks; the V^T operands come from transpose reads
@@ -566,8 +590,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
                     sa += x;
                     mx = fmaxf(mx, x);
                 }
-            mx = fmaxf(mx, xor32f(mx));
-            const float l_tot = l_run + xor32f(l_run);
+            const f32x2 mp = with_partner(mx), lp = with_partner(l_run);
+            mx = fmaxf(mp.x, mp.y);
+            const float l_tot = lp.x + lp.y;
             const bool ok = __builtin_isfinite(sa) && __builtin_isfinite(l_tot) &&
                             mx >= 0x1p-12f * l_tot;
             const bool live = p0 - P + col < n && seq_ok;
@@ -580,7 +605,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     }
 
     // ---- normalise and write this lane's query row ----
-    const float l_tot = l_run + xor32f(l_run);
+    const f32x2 lp = with_partner(l_run);
+    const float l_tot = lp.x + lp.y;
     const int64_t r = p0 - P + col;
     if (!wave_on || r >= n) return;
     const float inv = seq_ok ? 1.0f / l_tot : __builtin_nanf("");
