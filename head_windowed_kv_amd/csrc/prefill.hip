@@ -413,11 +413,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             // the row sum of the fp16 weights the P.V product uses, in fp32
             // (v_dot2_f32_f16 against (1, 1))
             const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-            float q0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[0]), one2, 0.f, false);
-            float q1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[2]), one2, 0.f, false);
-            q0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[1]), one2, q0, false);
-            q1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[3]), one2, q1, false);
-            psum += q0 + q1;
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[e]), one2, psum, false);
         } else {
             psum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         }
