@@ -263,7 +263,8 @@ def test_exact_variant_and_fp16_p_error(d, G):
     assert err_f <= BF16_TOL
 
 
-def test_v_beyond_fp16_range_falls_back_to_exact():
+@pytest.mark.parametrize("d", [128, 64, 256])
+def test_v_beyond_fp16_range_falls_back_to_exact(d):
     """V elements of +-2^20 (finite in bf16, beyond fp16's 65504) in the
     history and in the chunk: the fp16 pass of every workgroup that reads them
     turns non-finite, so those workgroups redo their rows exactly; all rows
@@ -279,10 +280,10 @@ def test_v_beyond_fp16_range_falls_back_to_exact():
         if p0 < P:  # history rows
             v[hist_pos - p0, 0, 3] = big
         else:       # chunk rows
-            v[chunk_row, 1, 7] = -big
+            v[chunk_row, 1, d - 7] = -big
 
-    say("prefill V beyond fp16 range")
-    c = PrefillCase([64, 500, 16, 2000], 128, 3, [P, 700], n, seed=460, v_edit=edit)
+    say("prefill V beyond fp16 range", d)
+    c = PrefillCase([64, 500, 16, 2000], d, 3, [P, 700], n, seed=460, v_edit=edit)
     out = c.run()
     got = to_host_f64(out)
     _check(got, c.oracle())
@@ -294,7 +295,8 @@ def test_v_beyond_fp16_range_falls_back_to_exact():
     assert torch.equal(out[0, chunk_row:, 3:6], exact[0, chunk_row:, 3:6])
 
 
-def test_tiny_v_falls_back_to_exact():
+@pytest.mark.parametrize("d", [128, 64, 256])
+def test_tiny_v_falls_back_to_exact(d):
     """V of kv head 1 scaled by 2^-20 (|v| ~ 1e-6: normal in bf16, subnormal
     in fp16): its outputs are far below 2^-12, so its workgroups redo their
     rows exactly (bit for bit the exact variant) while the other heads keep
@@ -302,8 +304,8 @@ def test_tiny_v_falls_back_to_exact():
     def edit(v, b, p0):
         v[..., 1, :] *= 2.0 ** -20
 
-    say("prefill tiny V")
-    c = PrefillCase([300, 2000, 64], 128, 2, [1500, 40], 96, seed=470, v_edit=edit)
+    say("prefill tiny V", d)
+    c = PrefillCase([300, 2000, 64], d, 2, [1500, 40], 96, seed=470, v_edit=edit)
     out = c.run()
     _check(to_host_f64(out), c.oracle())
     exact = c.run(exact=True)
