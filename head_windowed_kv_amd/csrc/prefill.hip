@@ -13,7 +13,8 @@
 //                 (row-major in LDS), B = Q^T held in registers; lane l then
 //                 owns query column l%32 and 16 of the 32 keys, so the
 //                 softmax over keys is in-lane plus one exchange with l^32.
-//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T read from the key-major V
+//   O^T = V^T P^T v_mfma_f32_32x32x16_f16 (bf16 in the exact form, below),
+//                 A = V^T read from the key-major V
 //                 tile with ds_read_b64_tr_b16 (the transpose happens in the
 //                 LDS read), B = P^T taken straight from the S^T registers; the
 //                 key order of the two operands is matched through the
