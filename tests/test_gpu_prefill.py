@@ -310,3 +310,14 @@ def test_tiny_v_falls_back_to_exact(d):
     _check(to_host_f64(out), c.oracle())
     exact = c.run(exact=True)
     assert torch.equal(out[:, :, 2:4], exact[:, :, 2:4])
+
+
+@pytest.mark.parametrize("n,pos0", [(1, [0, 5, 4096]), (2, [1, 17, 300]), (33, [0, 64, 1000])])
+def test_tiny_chunks(n, pos0):
+    """Chunks of 1, 2 and 33 rows (one workgroup, mostly idle waves; a single
+    row at P = 0 attends to itself only), both precisions."""
+    say("prefill tiny chunk", n, pos0)
+    c = PrefillCase([1, 100, 2000], 128, 3, pos0, n, seed=480 + n)
+    ref = c.oracle()
+    _check(to_host_f64(c.run()), ref)
+    assert row_rel_err(to_host_f64(c.run(exact=True)), ref) <= EXACT_TOL
