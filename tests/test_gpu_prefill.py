@@ -321,3 +321,51 @@ def test_tiny_chunks(n, pos0):
     ref = c.oracle()
     _check(to_host_f64(c.run()), ref)
     assert row_rel_err(to_host_f64(c.run(exact=True)), ref) <= EXACT_TOL
+
+
+def test_prefill_graph_replays_match_eager():
+    """Both prefill entries captured in one HIP graph (a workgroup of the
+    default entry redoes its rows exactly when it meets the V value beyond
+    fp16's range): three replays, with eager work and synchronisations in
+    between, each bit-identical to the eager calls."""
+    H = hw()
+    dev = device()
+    big = 2.0 ** 20
+
+    def edit(v, b, p0):
+        if b == 0 and p0 < 900:
+            v[900 - 3 - p0, 1, 5] = big
+
+    say("prefill graph replays")
+    c = PrefillCase([64, 500, 2000], 128, 3, [900, 40], 130, seed=490, v_edit=edit)
+    pos = torch.tensor(c.pos0, device=dev)
+    shape = (len(c.pos0), c.n, c.n_kv * c.G, c.d)
+    o_fast = torch.zeros(shape, dtype=torch.float32, device=dev)
+    o_exact = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(c.d)
+
+    def calls():
+        H.hwkv_prefill_attn(c.cache, 0, pos, c.q, c.k, c.v, o_fast, scale)
+        H.hwkv_prefill_attn_exact(c.cache, 0, pos, c.q, c.k, c.v, o_exact, scale)
+
+    calls()
+    torch.cuda.synchronize()
+    want_fast, want_exact = o_fast.clone(), o_exact.clone()
+    _check(to_host_f64(want_fast), c.oracle())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()  # warm the launch path on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        o_fast.fill_(float("nan"))
+        o_exact.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_fast, want_fast), rep
+        assert torch.equal(o_exact, want_exact), rep
