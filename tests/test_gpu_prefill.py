@@ -369,3 +369,25 @@ def test_prefill_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(o_fast, want_fast), rep
         assert torch.equal(o_exact, want_exact), rep
+
+
+def test_invalid_slot_and_negative_position_give_nan_rows():
+    """A slot outside the block table, or pos0 < 0, makes that sequence's rows
+    NaN (nothing outside the table or pool is read); the other sequences'
+    rows are bit-identical to a call with valid arguments."""
+    H = hw()
+    dev = device()
+    say("prefill invalid slot / position")
+    c = PrefillCase([64, 700], 128, 3, [500, 300, 900], 40, seed=495)
+    good = c.run()
+    scale = 1.0 / math.sqrt(c.d)
+    for slots, pos0, bad in (([0, 7, 2], c.pos0, 1), ([0, 1, 2], [500, -3, 900], 1),
+                             ([-1, 1, 2], c.pos0, 0)):
+        out = torch.zeros_like(good)
+        H.hwkv_prefill_attn(c.cache, 0, torch.tensor(pos0, device=dev), c.q, c.k, c.v, out,
+                            scale, seq_slots=torch.tensor(slots, dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+        assert torch.all(torch.isnan(out[bad])), (slots, pos0)
+        for b in range(3):
+            if b != bad:
+                assert torch.equal(out[b], good[b]), (slots, pos0, b)
