@@ -304,7 +304,10 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * [head_dim] as out_dtype (F32, BF16 or F16).  The cache is read, not written: call hwkv_append
  * with the same k, v (n_layers = 1) afterwards, since appending first could
  * overwrite history that earlier rows of the chunk still need.  Runs on
- * MFMA tiles (bf16 or fp16 operands, fp32 accumulation).
+ * MFMA tiles (bf16 or fp16 operands, fp32 accumulation).  A sequence whose
+ * slot lies outside the block table, or whose pos0 is negative, gets NaN
+ * rows and reads nothing outside the table or pool; block ids outside the
+ * pool are read as block 0.
  *
  * Precision of the softmax weights P in the P.V product: they are rounded
  * once to fp16 (11 significant bits; row error a few 1e-4 of the row's
