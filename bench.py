@@ -586,7 +586,8 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
         meta_host = H.hwkv_meta_fill(lay)
         meta = H._alloc_aligned(meta_host.size, dev)
         meta.copy_(torch.from_numpy(meta_host))
-        cache = H.Cache(lay, cache.pool, cache.block_ids, meta)
+        cache = H.Cache(lay, cache.pool, cache.block_ids, meta,
+                        H.hwkv_meta_fingerprint(meta_host))
     pos = torch.full((n_seqs,), L, dtype=torch.int64, device=dev)
     ctx = torch.full((n_seqs,), L + 1, dtype=torch.int64, device=dev)
     mk = H.make_step_workspace if mode == "single_launch" else H.make_workspace

@@ -29,7 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 HWKV_F32 = 0
 HWKV_BF16 = 1
 HWKV_F16 = 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS_NAMES = {0: "HWKV_OK", 1: "HWKV_ERR_INVALID_ARG", 2: "HWKV_ERR_UNSUPPORTED",
                 3: "HWKV_ERR_MISALIGNED", 4: "HWKV_ERR_CAPACITY", 5: "HWKV_ERR_ABI_MISMATCH",
@@ -38,7 +38,7 @@ STATUS_NAMES = {0: "HWKV_OK", 1: "HWKV_ERR_INVALID_ARG", 2: "HWKV_ERR_UNSUPPORTE
 #: every symbol the C ABI exports
 EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_layout_destroy",
             "hwkv_layout_query", "hwkv_mem_estimate", "hwkv_capacity_check", "hwkv_table_fill",
-            "hwkv_meta_fill",
+            "hwkv_meta_fill", "hwkv_meta_fingerprint",
             "hwkv_workspace_bytes", "hwkv_append", "hwkv_decode_split", "hwkv_decode_merge",
             "hwkv_decode_attn", "hwkv_decode_split_append", "hwkv_decode_append_attn",
             "hwkv_step_workspace_bytes",
@@ -59,7 +59,7 @@ class hwkv_layout_desc(ctypes.Structure):
 class hwkv_cache(ctypes.Structure):
     _fields_ = [("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64),
                 ("block_ids", ctypes.c_void_p), ("table_rows", ctypes.c_int64),
-                ("meta", ctypes.c_void_p)]
+                ("meta", ctypes.c_void_p), ("meta_fingerprint", ctypes.c_uint64)]
 
 
 _i32, _i64, _u64, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
@@ -84,6 +84,8 @@ _lib.hwkv_table_fill.restype = ctypes.c_int
 _lib.hwkv_table_fill.argtypes = [_vp, _i64, _vp]
 _lib.hwkv_meta_fill.restype = ctypes.c_int
 _lib.hwkv_meta_fill.argtypes = [_vp, _vp, _u64]
+_lib.hwkv_meta_fingerprint.restype = ctypes.c_int
+_lib.hwkv_meta_fingerprint.argtypes = [_vp, _u64, _P(_u64)]
 _lib.hwkv_workspace_bytes.restype = ctypes.c_int
 _lib.hwkv_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _i32, _P(_u64)]
 _lib.hwkv_append.restype = ctypes.c_int
@@ -233,6 +235,14 @@ def hwkv_meta_fill(layout: Layout) -> np.ndarray:
     return buf
 
 
+def hwkv_meta_fingerprint(meta_host: np.ndarray) -> int:
+    """The layout fingerprint a host copy of a meta blob carries."""
+    buf = np.ascontiguousarray(meta_host, dtype=np.uint8)
+    fp = ctypes.c_uint64()
+    _check(_lib.hwkv_meta_fingerprint(buf.ctypes.data_as(_vp), buf.size, ctypes.byref(fp)))
+    return int(fp.value)
+
+
 def hwkv_workspace_bytes(layout: Layout, layer_begin: int, n_layers: int, n_seqs: int,
                          n_q_heads: int) -> int:
     b = ctypes.c_uint64()
@@ -259,6 +269,7 @@ class Cache:
     pool: torch.Tensor        # uint8 [pool_bytes]
     block_ids: torch.Tensor   # int32 [table_rows][blocks_per_seq]
     meta: torch.Tensor        # uint8 [meta_bytes]
+    meta_fingerprint: int = 0  # fingerprint the blob carries (hwkv_meta_fingerprint)
 
     @property
     def table_rows(self) -> int:
@@ -266,7 +277,7 @@ class Cache:
 
     def view(self) -> hwkv_cache:
         return hwkv_cache(self.pool.data_ptr(), self.pool.numel(), self.block_ids.data_ptr(),
-                          self.table_rows, self.meta.data_ptr())
+                          self.table_rows, self.meta.data_ptr(), self.meta_fingerprint)
 
 
 def make_cache(layout: Layout, n_seqs: int, device="cuda", block_ids: Optional[np.ndarray] = None,
@@ -286,7 +297,7 @@ def make_cache(layout: Layout, n_seqs: int, device="cuda", block_ids: Optional[n
     meta_host = hwkv_meta_fill(layout)
     meta = _alloc_aligned(meta_host.size, device)
     meta.copy_(torch.from_numpy(meta_host))
-    return Cache(layout, pool, tbl, meta)
+    return Cache(layout, pool, tbl, meta, hwkv_meta_fingerprint(meta_host))
 
 
 def make_workspace(layout: Layout, layer_begin: int, n_layers: int, n_seqs: int, n_q_heads: int,

@@ -16,6 +16,21 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+std::string hex64(uint64_t x) {
+    static const char* digits = "0123456789abcdef";
+    std::string s = "0x";
+    for (int i = 60; i >= 0; i -= 4) s += digits[(x >> i) & 15];
+    return s;
+}
+
+// the softmax scale: finite and positive (a non-positive scale would turn
+// the masked scores' -inf into +inf or NaN in the kernels' log2 domain)
+hwkv_status check_scale(float scale) {
+    if (!(isfinite(scale) && scale > 0.f))
+        return fail(HWKV_ERR_INVALID_ARG, "scale must be finite and > 0");
+    return HWKV_OK;
+}
+
 // Checks shared by every device call: the cache view, its alignment and the
 // pool capacity.  A pool smaller than the exact estimate for table_rows rows
 // is reported in the form of the write-up's operations table, naming the first
@@ -28,11 +43,21 @@ hwkv_status check_cache(const hwkv_layout* L, const hwkv_cache* c) {
     if (!aligned(c->pool, 256) || !aligned(c->block_ids, 256) || !aligned(c->meta, 256))
         return fail(HWKV_ERR_MISALIGNED, "pool, block_ids and meta must be 256-byte aligned");
     if (c->table_rows < 1) return fail(HWKV_ERR_INVALID_ARG, "table_rows must be >= 1");
+    // kernel-ABI check ("KV Cache Management in Hybrid Attention LLMs", 4.2):
+    // the cache's blob must have been written for this very layout
+    if (c->meta_fingerprint != L->fingerprint)
+        return fail(HWKV_ERR_ABI_MISMATCH,
+                    "the cache's meta blob has fingerprint " + hex64(c->meta_fingerprint) +
+                        ", the layout of this call " + hex64(L->fingerprint) +
+                        " (another layout, or another ABI version)");
     return hwkv_capacity_check(L, c->table_rows, c->pool_bytes, nullptr, nullptr, nullptr);
 }
 
+// reads_table: the call looks rows up in the block table (every stage except
+// the merge, which reads only the workspace and the contexts)
 hwkv_status check_batch(const hwkv_layout* L, const hwkv_cache* c, int32_t layer_begin,
-                        int32_t n_layers, int32_t n_seqs, const int32_t* seq_slots) {
+                        int32_t n_layers, int32_t n_seqs, const int32_t* seq_slots,
+                        bool reads_table = true) {
     if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > L->n_layers)
         return fail(HWKV_ERR_INVALID_ARG, "layer range [" + std::to_string(layer_begin) + ", " +
                                               std::to_string(layer_begin + n_layers) +
@@ -40,7 +65,7 @@ hwkv_status check_batch(const hwkv_layout* L, const hwkv_cache* c, int32_t layer
                                               std::to_string(L->n_layers) + " layers");
     if (n_seqs < 1 || n_seqs > 65535)
         return fail(HWKV_ERR_INVALID_ARG, "n_seqs must be in [1, 65535]");
-    if (!seq_slots && n_seqs > c->table_rows)
+    if (reads_table && !seq_slots && n_seqs > c->table_rows)
         return fail(HWKV_ERR_INVALID_ARG, "no seq_slots and n_seqs > table_rows");
     if (seq_slots && !aligned(seq_slots, 4))
         return fail(HWKV_ERR_MISALIGNED, "seq_slots must be 4-byte aligned");
@@ -141,7 +166,7 @@ static hwkv_status split_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
     if (!ctx_len || !q) return fail(HWKV_ERR_INVALID_ARG, "null ctx_len or q");
     if (!aligned(ctx_len, 8)) return fail(HWKV_ERR_MISALIGNED, "ctx_len must be 8-byte aligned");
     if (!aligned(q, 16)) return fail(HWKV_ERR_MISALIGNED, "q must be 16-byte aligned");
-    if (!isfinite(scale)) return fail(HWKV_ERR_INVALID_ARG, "scale must be finite");
+    HWKV_TRY(check_scale(scale));
     *a = DecodeSplitArgs{};
     a->pool = static_cast<const uint8_t*>(c->pool);
     a->n_pool_blocks = pool_blocks(L, c);
@@ -176,7 +201,7 @@ static hwkv_status merge_args(const hwkv_layout* L, const hwkv_cache* c, int32_t
                               int32_t n_q_heads, const void* ws, uint64_t ws_bytes, void* out,
                               hwkv_dtype out_dtype, int* group, DecodeMergeArgs* a) {
     HWKV_TRY(check_cache(L, c));
-    HWKV_TRY(check_batch(L, c, layer_begin, n_layers, n_seqs, nullptr));
+    HWKV_TRY(check_batch(L, c, layer_begin, n_layers, n_seqs, nullptr, false));
     HWKV_TRY(check_group(L, n_q_heads, group));
     if (!decode_supported(*L, *group))
         return fail(HWKV_ERR_UNSUPPORTED, "no decode kernel for this block size, dtype, head_dim "
@@ -284,13 +309,12 @@ hwkv_status hwkv_decode_split_append(const hwkv_layout* L, const hwkv_cache* c,
     return launch_decode_split_append(*L, group, sa, stream);
 }
 
-hwkv_status hwkv_decode_append_attn(const hwkv_layout* L, const hwkv_cache* c,
-                                    int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
-                                    const int32_t* seq_slots, const int64_t* pos,
-                                    const void* k_new, const void* v_new, int32_t n_q_heads,
-                                    const void* q, float scale, void* ws, uint64_t ws_bytes,
-                                    void* out, hwkv_dtype out_dtype, hipStream_t stream) {
-    clear_error();
+static hwkv_status decode_append_attn(const hwkv_layout* L, const hwkv_cache* c,
+                                      int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                      const int32_t* seq_slots, const int64_t* pos,
+                                      const void* k_new, const void* v_new, int32_t n_q_heads,
+                                      const void* q, float scale, void* ws, uint64_t ws_bytes,
+                                      void* out, hwkv_dtype out_dtype, hipStream_t stream) {
     int group = 0;
     DecodeSplitArgs sa;
     DecodeMergeArgs ma;
@@ -302,6 +326,17 @@ hwkv_status hwkv_decode_append_attn(const hwkv_layout* L, const hwkv_cache* c,
     ma.ctx_add = 1;
     HWKV_TRY(launch_decode_split_append(*L, group, sa, stream));
     return launch_decode_merge(*L, group, ma, stream);
+}
+
+hwkv_status hwkv_decode_append_attn(const hwkv_layout* L, const hwkv_cache* c,
+                                    int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                    const int32_t* seq_slots, const int64_t* pos,
+                                    const void* k_new, const void* v_new, int32_t n_q_heads,
+                                    const void* q, float scale, void* ws, uint64_t ws_bytes,
+                                    void* out, hwkv_dtype out_dtype, hipStream_t stream) {
+    clear_error();
+    return decode_append_attn(L, c, layer_begin, n_layers, n_seqs, seq_slots, pos, k_new, v_new,
+                              n_q_heads, q, scale, ws, ws_bytes, out, out_dtype, stream);
 }
 
 hwkv_status hwkv_decode_step(const hwkv_layout* L, const hwkv_cache* c, int32_t layer_begin,
@@ -359,7 +394,7 @@ static hwkv_status prefill_entry(const hwkv_layout* L, const hwkv_cache* c, int3
         return fail(HWKV_ERR_MISALIGNED, "q, k, v and out must be 16-byte aligned");
     if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16 && out_dtype != HWKV_F16)
         return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32, HWKV_BF16 or HWKV_F16");
-    if (!isfinite(scale)) return fail(HWKV_ERR_INVALID_ARG, "scale must be finite");
+    HWKV_TRY(check_scale(scale));
     PrefillArgs a{};
     a.pool = static_cast<const uint8_t*>(c->pool);
     a.n_pool_blocks = pool_blocks(L, c);

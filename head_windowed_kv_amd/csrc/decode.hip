@@ -608,7 +608,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     }
 
     const uint64_t nblk_pool = a.n_pool_blocks;
-    // physical block i of this wave (block 0 stands in for an invalid id)
+    // physical block i of this wave.  Block 0 stands in for an id outside
+    // the pool, so the loads stay in bounds; every block of a split holds
+    // tokens of the window, so such an id makes the head's result NaN (the
+    // fold poisons the running sum l).
     auto block_ptr = [&](int i, bool& ok) -> const uint8_t* {
         const int32_t id = __builtin_amdgcn_readlane(my_id, i);
         ok = id >= 0 && (uint64_t)id < nblk_pool;
@@ -646,6 +649,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
                 valid[rho] = ok && pos >= lo && pos < L;
             }
             process_block<T, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
+            if (!ok) {  // an id outside the pool: NaN for every query head of the group
+#pragma unroll
+                for (int h = 0; h < G; h++) l[h] = __builtin_nanf("");
+            }
         }
     };
 

@@ -309,6 +309,24 @@ hwkv_status hwkv_meta_fill(const hwkv_layout* L, void* meta_host, uint64_t meta_
     return HWKV_OK;
 }
 
+hwkv_status hwkv_meta_fingerprint(const void* meta_host, uint64_t meta_bytes,
+                                  uint64_t* fingerprint) {
+    clear_error();
+    if (!meta_host || !fingerprint) return fail(HWKV_ERR_INVALID_ARG, "null argument");
+    if (meta_bytes < sizeof(MetaHeader))
+        return fail(HWKV_ERR_INVALID_ARG, "a meta blob is at least " +
+                                              std::to_string(sizeof(MetaHeader)) + " bytes");
+    MetaHeader hdr;
+    memcpy(&hdr, meta_host, sizeof hdr);
+    if (hdr.magic != kMetaMagic) return fail(HWKV_ERR_ABI_MISMATCH, "not a meta blob");
+    if (hdr.abi != HWKV_ABI_VERSION)
+        return fail(HWKV_ERR_ABI_MISMATCH, "meta blob written under ABI version " +
+                                               std::to_string(hdr.abi) + ", this library is " +
+                                               std::to_string(HWKV_ABI_VERSION));
+    *fingerprint = hdr.fingerprint;
+    return HWKV_OK;
+}
+
 hwkv_status hwkv_workspace_bytes(const hwkv_layout* L, int32_t layer_begin, int32_t n_layers,
                                  int32_t n_seqs, int32_t n_q_heads, uint64_t* bytes) {
     clear_error();

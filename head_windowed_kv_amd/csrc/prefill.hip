@@ -183,6 +183,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TILE];
     __shared__ int s_redo;  // a workgroup's fp16 pass must be redone exactly
+    // per wave: the last history key position it staged from a block whose
+    // id lies outside the pool; the rows whose window reaches it are NaN
+    __shared__ int64_t s_bad_hi[kWaves];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,10 +205,26 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     const int in_xcd = blockIdx.x / kXcds;
     const int pair = (in_xcd / n_groups) * kXcds + xcd;
     const int ug = in_xcd % n_groups;
-    if (pair >= a.n_kv_heads * a.n_seqs) return;
 
     const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
-    if (fp != a.fingerprint) return;
+    if (fp != a.fingerprint) {
+        // a meta blob of another layout: its head table cannot be trusted,
+        // so the whole grid writes NaN over the whole output
+        const int64_t n4 = (int64_t)a.n_seqs * n * a.n_q_heads * (D / 4);
+        const float x = __builtin_nanf("");
+        for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n4;
+             e += (int64_t)gridDim.x * kThreads) {
+            if (a.out_kind == kBF16 || a.out_kind == kF16)
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + e * 4) =
+                    a.out_kind == kBF16 ? u32x2{pack_bf16(x, x), pack_bf16(x, x)}
+                                        : u32x2{pack_f16(x, x), pack_f16(x, x)};
+            else
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + e * 4) =
+                    f32x4{x, x, x, x};
+        }
+        return;
+    }
+    if (pair >= a.n_kv_heads * a.n_seqs) return;
     if (threadIdx.x == 0) s_redo = 0;  // read only after later barriers
     const int rank = pair / a.n_seqs;
     const int b = pair % a.n_seqs;
@@ -255,16 +274,28 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     auto xv = [](int j) -> uint32_t { return (uint32_t)((swz_v<D>(C::RPI * j) ) * 16); };
     const int64_t pool_blocks = (int64_t)a.n_pool_blocks;
 
+    // last key of a lost history slice this wave staged (wave-uniform); the
+    // start value lies below every window start, positions included
+    constexpr int64_t kNoBadKey = -(int64_t(1) << 62);
+    int64_t bad_hi = kNoBadKey;
     const int tpb_log2 = BIG ? a.tpb_log2 : 0;  // 16-key slices per cache block = 1 << tpb_log2
     const uint32_t vhalf = ((uint32_t)kBS << tpb_log2) * C::ROW;  // K half of a cache block
     auto issue = [&](uint8_t* slot_base, int64_t X, int32_t id, bool is_v) {
         uint8_t* dst = slot_base + wave * (kBS * C::ROW);
         const int64_t tb = X * kBK + wave * kBS;  // first key of the slice
         const uint32_t sub = ((uint32_t)X * (kBK / kBS) + wave) & ((1u << tpb_log2) - 1u);
-        const int64_t idc = (id >= 0 && id < pool_blocks) ? id : 0;
+        const bool id_ok = id >= 0 && id < pool_blocks;
+        // an id outside the pool reads zeros (an empty buffer range), so the
+        // rows that mask its keys out see exact zeros, never stale bytes
+        const int64_t idc = id_ok ? id : 0;
+        if (!id_ok && tb < P) {
+            // history keys [tb, min(tb + 16, P)) of this slice are lost
+            const int64_t last = (tb + kBS < P ? tb + kBS : P) - 1;
+            bad_hi = last > bad_hi ? last : bad_hi;
+        }
         const rsrc_t rh = make_rsrc(a.pool + idc * a.block_bytes +
                                         ((is_v ? vhalf : 0u) + sub * (kBS * C::ROW)),
-                                    kBS * C::ROW);
+                                    id_ok ? kBS * C::ROW : 0u);
         const uint8_t* cbase = is_v ? vc_base : kc_base;
         if (tb + kBS <= P) {  // history block: every row from the ring block
 #pragma unroll
@@ -604,11 +635,19 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     }
 
     // ---- normalise and write this lane's query row ----
+    if (lane == 0) s_bad_hi[wave] = bad_hi;
+    __syncthreads();
+    int64_t lost = s_bad_hi[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; i++) lost = s_bad_hi[i] > lost ? s_bad_hi[i] : lost;
     const f32x2 lp = with_partner(l_run);
     const float l_tot = lp.x + lp.y;
     const int64_t r = p0 - P + col;
     if (!wave_on || r >= n) return;
-    const float inv = seq_ok ? 1.0f / l_tot : __builtin_nanf("");
+    // NaN for a bad sequence, and for a row whose window [p - w + 1, p]
+    // reaches a history key held by a block outside the pool
+    const bool row_ok = seq_ok && lost < p0 + col - w + 1;
+    const float inv = row_ok ? 1.0f / l_tot : __builtin_nanf("");
     const int64_t obase = (((int64_t)b * n + r) * a.n_q_heads + (int64_t)kvh * G + qg) * D;
 #pragma unroll
     for (int db = 0; db < C::DBLK; db++)

@@ -34,6 +34,35 @@
  *     pool, block table, meta and workspace pointers must be 256-byte aligned;
  *     q, k, v and out 16-byte aligned (128-bit accesses); ctx_len/pos0 8-byte
  *     and seq_slots 4-byte aligned.  Violations return HWKV_ERR_MISALIGNED.
+ *   - Kernel-ABI check (same page, section 4.2: a kernel must only read a
+ *     cache whose layout it was built for): the meta blob carries the ABI
+ *     version and the layout fingerprint, and the cache view states which
+ *     fingerprint its blob holds (hwkv_cache.meta_fingerprint).  Every device
+ *     call returns HWKV_ERR_ABI_MISMATCH, before enqueueing anything, when
+ *     that differs from the fingerprint of the layout it is called with.
+ *     The kernels compare the blob itself as well (a view that misstates its
+ *     blob): see "Bad device values" below.
+ *   - The softmax scale of the attention calls must be finite and > 0
+ *     (HWKV_ERR_INVALID_ARG otherwise).
+ *
+ * Bad device values.  Device arrays (seq_slots, positions, block ids, the
+ * meta blob) are the caller's contract; the kernels never trust them for
+ * addressing (nothing is read or written outside the pool, the table or the
+ * caller's tensors) and turn each violation into a visible result, the same
+ * in every kernel:
+ *   - a slot outside [0, table_rows): append writes nothing for that
+ *     sequence; attention gives NaN rows for it;
+ *   - a negative position: append writes nothing for that sequence; decode
+ *     (context <= 0) gives zero rows; prefill (pos0 < 0) gives NaN rows;
+ *   - a block id outside the pool: append skips the rows that map to it;
+ *     an attention query row whose window holds a key stored in that block
+ *     comes out NaN (in decode one query row reads the whole window, so all
+ *     G query heads of that (sequence, kv head) are NaN; in prefill exactly
+ *     the chunk rows whose window reaches that block's keys);
+ *   - a meta blob of another layout: append writes nothing; attention writes
+ *     NaN over its whole output.
+ * The write-up's troubleshooting row locates failures by (layer, head): a
+ * NaN output row names them through its position in out.
  *
  * Memory layout of the pool.  Physical block i occupies bytes
  * [i*block_bytes, (i+1)*block_bytes): first block_size K rows of head_dim
@@ -56,7 +85,7 @@
 extern "C" {
 #endif
 
-#define HWKV_ABI_VERSION 1u
+#define HWKV_ABI_VERSION 2u
 
 typedef enum hwkv_status {
     HWKV_OK = 0,
@@ -101,11 +130,17 @@ typedef struct hwkv_cache {
     const int32_t *block_ids; /* device [table_rows][blocks_per_seq], 256-B aligned */
     int64_t table_rows;       /* number of sequence rows (cache slots) */
     const void *meta;         /* device copy of hwkv_meta_fill, 256-B aligned */
+    uint64_t meta_fingerprint; /* fingerprint the blob at meta carries: the
+                                  hwkv_layout_desc.fingerprint of the layout
+                                  that wrote it (hwkv_meta_fingerprint reads it
+                                  from a host copy) */
 } hwkv_cache;
 
 /* ABI version compiled into the library (== HWKV_ABI_VERSION of its header).
- * Page 1 (section 4.2) asks that a kernel reading a cache match the layout of
- * the kernel that wrote it; callers compare this and the layout fingerprint. */
+ * "KV Cache Management in Hybrid Attention LLMs", section 4.2, asks that a
+ * kernel reading a cache match the layout of the kernel that wrote it;
+ * callers compare this, and the device calls compare the layout
+ * fingerprint. */
 uint32_t hwkv_abi_version(void);
 
 /* Message of the last failing call on this thread ("" if none).  Capacity
@@ -162,22 +197,40 @@ hwkv_status hwkv_capacity_check(const hwkv_layout *layout, int64_t n_seqs,
 
 /* Default block tables into host memory block_ids[n_seqs*blocks_per_seq]:
  * row s gets the consecutive ids [s*blocks_per_seq, (s+1)*blocks_per_seq).
- * OVERFLOW if an id would not fit int32. */
+ * This is the per-head BlockTable of the write-up's 核心技术 2 ("Grouped-Cache
+ * Runtime": each head's table holds ceil(window / block_size) blocks), with
+ * the heads of a sequence laid end to end in layer-major order; any other
+ * assignment of distinct ids inside the pool is equally valid.  OVERFLOW if
+ * an id would not fit int32. */
 hwkv_status hwkv_table_fill(const hwkv_layout *layout, int64_t n_seqs,
                             int32_t *block_ids);
 
 /* Write the layout's device descriptor blob (per-head windows, block counts,
  * table offsets and the decode work list) into host memory meta_host of
  * meta_bytes >= desc.meta_bytes.  The caller copies it to device memory once
- * and passes that copy as hwkv_cache.meta.  The blob carries the ABI version
- * and the layout fingerprint; kernels given a blob of another layout write
- * nothing (append) or NaN (attention). */
+ * and passes that copy as hwkv_cache.meta, with hwkv_cache.meta_fingerprint
+ * set to the layout's fingerprint.  The blob carries the ABI version and the
+ * fingerprint ("KV Cache Management in Hybrid Attention LLMs", section 4.2:
+ * kernel-ABI check); kernels given a blob of another layout write nothing
+ * (append) or NaN (attention). */
 hwkv_status hwkv_meta_fill(const hwkv_layout *layout, void *meta_host,
                            uint64_t meta_bytes);
 
+/* The fingerprint a meta blob carries, read from a host copy of it (e.g. a
+ * blob kept with a cache that is restored later): *fingerprint receives the
+ * hwkv_layout_desc.fingerprint of the layout that wrote it.  INVALID_ARG for
+ * a null pointer or a buffer shorter than the blob header; ABI_MISMATCH when
+ * the buffer is not a meta blob or was written under another ABI version. */
+hwkv_status hwkv_meta_fingerprint(const void *meta_host, uint64_t meta_bytes,
+                                  uint64_t *fingerprint);
+
 /* Device workspace needed by hwkv_decode_split/_merge/_attn for layers
  * [layer_begin, layer_begin+n_layers), n_seqs sequences and n_q_heads query
- * heads: one fp32 record (acc[G][d], m[G], l[G]) per (sequence, work item). */
+ * heads: one fp32 record (acc[G][d], m[G], l[G]) per (sequence, work item).
+ * The pages fix what decode computes (softmax over each head's window,
+ * 摘要 and 核心技术 2) but not how; the workspace belongs to this library's
+ * split-K form of it: the window of a head is cut into splits whose partial
+ * softmax states are merged exactly, in a fixed order. */
 hwkv_status hwkv_workspace_bytes(const hwkv_layout *layout, int32_t layer_begin,
                                  int32_t n_layers, int32_t n_seqs,
                                  int32_t n_q_heads, uint64_t *bytes);
@@ -206,7 +259,8 @@ hwkv_status hwkv_append(const hwkv_layout *layout, const hwkv_cache *cache,
  * running max m, sum l and acc = sum_t 2^(s_t-m) v_t for the G = n_q_heads /
  * n_kv_heads query heads of the group (query head i reads kv head i / G),
  * s_t = log2(e) * scale * q_i . k_t.  q: device [n_layers][n_seqs][n_q_heads]
- * [head_dim] in the layout's dtype.  workspace: hwkv_workspace_bytes. */
+ * [head_dim] in the layout's dtype.  workspace: hwkv_workspace_bytes.
+ * scale: finite and > 0. */
 hwkv_status hwkv_decode_split(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer_begin, int32_t n_layers,
                               int32_t n_seqs, const int32_t *seq_slots,
@@ -219,7 +273,9 @@ hwkv_status hwkv_decode_split(const hwkv_layout *layout, const hwkv_cache *cache
  * out: device [n_layers][n_seqs][n_q_heads][head_dim] as out_dtype (F32, or
  * BF16 / F16 rounded to nearest even from fp32).  A sequence with
  * ctx_len <= 0 gets zeros.  Same layer range, n_seqs, ctx_len
- * and workspace as the split stage. */
+ * and workspace as the split stage (the merge reads only the workspace and
+ * ctx_len, so n_seqs may exceed the table's rows, as a split stage given
+ * seq_slots allows). */
 hwkv_status hwkv_decode_merge(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer_begin, int32_t n_layers,
                               int32_t n_seqs, const int64_t *ctx_len,
@@ -294,7 +350,10 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
                              uint64_t workspace_bytes, void *out, hwkv_dtype out_dtype,
                              hipStream_t stream);
 
-/* Chunked prefill of one layer: sequence b has history [0, P) in the cache,
+/* Chunked prefill of one layer.  The pages define the per-head window (摘要,
+ * 核心技术 2; "KV Cache Consistency Practices ...", "SWA Window") but no
+ * prefill kernel: this is the same windowed attention for a chunk of new
+ * query rows, causal inside the chunk.  Sequence b has history [0, P) in the cache,
  * P = pos0[b], and n_chunk new tokens at [P, P+n_chunk).  Query row r
  * (position p = P + r) of query head i attends to kv head i / G over
  * [max(0, p-w+1), p]: keys before P are read from the cache (only the last
@@ -304,10 +363,9 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * [head_dim] as out_dtype (F32, BF16 or F16).  The cache is read, not written: call hwkv_append
  * with the same k, v (n_layers = 1) afterwards, since appending first could
  * overwrite history that earlier rows of the chunk still need.  Runs on
- * MFMA tiles (bf16 or fp16 operands, fp32 accumulation).  A sequence whose
- * slot lies outside the block table, or whose pos0 is negative, gets NaN
- * rows and reads nothing outside the table or pool; block ids outside the
- * pool are read as block 0.
+ * MFMA tiles (bf16 or fp16 operands, fp32 accumulation).  scale: finite
+ * and > 0.  Bad slots, positions and block ids give NaN rows as stated at
+ * the top of this header.
  *
  * Precision of the softmax weights P in the P.V product: they are rounded
  * once to fp16 (11 significant bits; row error a few 1e-4 of the row's

@@ -86,8 +86,16 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
     EXPECT(hwkv_workspace_bytes(lay, 0, L, (int32_t)n_seqs, nq + 1, &ws) != HWKV_OK);
     EXPECT(hwkv_step_workspace_bytes(lay, 0, L, (int32_t)n_seqs, nq, &sws) == HWKV_OK);
 
+    uint64_t mfp = 0;
+    EXPECT(hwkv_meta_fingerprint(meta.data(), meta.size(), &mfp) == HWKV_OK);
+    EXPECT(mfp == desc.fingerprint);
+    EXPECT(hwkv_meta_fingerprint(meta.data(), 16, &mfp) == HWKV_ERR_INVALID_ARG);
+    EXPECT(hwkv_meta_fingerprint(nullptr, meta.size(), &mfp) == HWKV_ERR_INVALID_ARG);
+    std::vector<uint8_t> junk(meta.size(), 0);
+    EXPECT(hwkv_meta_fingerprint(junk.data(), junk.size(), &mfp) == HWKV_ERR_ABI_MISMATCH);
+
     hwkv_cache c = {fake<void>(1024), est, fake<const int32_t>(2048), n_seqs,
-                    fake<const void>(2049)};
+                    fake<const void>(2049), mfp};
     hwkv_cache small = c;
     small.pool_bytes = est - 1;
     void* wsp = fake<void>(4096);
@@ -118,6 +126,14 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
                              0.1f, nullptr) == HWKV_OK);
     EXPECT(hwkv_prefill_attn_exact(lay, &c, 0, ns, nullptr, pos, 1, nq, q, k, v, out, HWKV_F32,
                                    0.1f, nullptr) == HWKV_OK);
+    // the merge reads only the workspace and the contexts: a batch larger
+    // than the table (several entries reading one slot) is accepted
+    EXPECT(hwkv_decode_attn(lay, &c, 0, L, ns + 2, slots, pos, nq, q, 0.1f, wsp, 2 * ws, out,
+                            HWKV_F32, nullptr) == HWKV_OK);
+    EXPECT(hwkv_decode_merge(lay, &c, 0, L, ns + 2, pos, nq, wsp, 2 * ws, out, HWKV_F32,
+                             nullptr) == HWKV_OK);
+    EXPECT(hwkv_decode_append_attn(lay, &c, 0, L, ns + 2, slots, pos, k, v, nq, q, 0.1f, wsp,
+                                   2 * ws, out, HWKV_BF16, nullptr) == HWKV_OK);
     EXPECT(hwkv::g_launches > before);
 
     // rejected calls: nothing launched
@@ -139,6 +155,29 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
                                    0.1f, nullptr) != HWKV_OK);
     EXPECT(hwkv_prefill_attn(lay, nullptr, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, 0.1f,
                              nullptr) != HWKV_OK);
+    // a view whose blob belongs to another layout (kernel-ABI check)
+    hwkv_cache other = c;
+    other.meta_fingerprint ^= 1;
+    EXPECT(hwkv_append(lay, &other, 0, L, ns, slots, pos, 5, k, v, nullptr) ==
+           HWKV_ERR_ABI_MISMATCH);
+    EXPECT(hwkv_decode_attn(lay, &other, 0, L, ns, slots, pos, nq, q, 0.1f, wsp, ws, out,
+                            HWKV_F32, nullptr) == HWKV_ERR_ABI_MISMATCH);
+    EXPECT(hwkv_decode_merge(lay, &other, 0, L, ns, pos, nq, wsp, ws, out, HWKV_F32, nullptr) ==
+           HWKV_ERR_ABI_MISMATCH);
+    EXPECT(hwkv_decode_step(lay, &other, 0, L, ns, slots, pos, k, v, nq, q, 0.1f, wsp, sws, out,
+                            HWKV_F32, nullptr) == HWKV_ERR_ABI_MISMATCH);
+    EXPECT(hwkv_prefill_attn(lay, &other, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, 0.1f,
+                             nullptr) == HWKV_ERR_ABI_MISMATCH);
+    // the softmax scale must be finite and positive
+    const float bad_scales[3] = {0.0f, -0.5f, __builtin_nanf("")};
+    for (float sc : bad_scales) {
+        EXPECT(hwkv_decode_attn(lay, &c, 0, L, ns, slots, pos, nq, q, sc, wsp, ws, out, HWKV_F32,
+                                nullptr) == HWKV_ERR_INVALID_ARG);
+        EXPECT(hwkv_decode_step(lay, &c, 0, L, ns, slots, pos, k, v, nq, q, sc, wsp, sws, out,
+                                HWKV_F32, nullptr) == HWKV_ERR_INVALID_ARG);
+        EXPECT(hwkv_prefill_attn(lay, &c, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, sc,
+                                 nullptr) == HWKV_ERR_INVALID_ARG);
+    }
     EXPECT(hwkv::g_launches == mid);
     hwkv_layout_destroy(lay);
 }

@@ -39,7 +39,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert hw.hwkv_abi_version() == hw.ABI_VERSION == 1
+    # 2: hwkv_cache carries the fingerprint of its meta blob
+    assert hw.hwkv_abi_version() == hw.ABI_VERSION == 2
+    text = open(os.path.join(ROOT, "include", "hwkv.h")).read()
+    assert re.search(r"#define HWKV_ABI_VERSION %du\b" % hw.ABI_VERSION, text)
 
 
 @pytest.mark.parametrize("name", sorted(CONFIG_WINDOWS))
@@ -102,8 +105,28 @@ def test_meta_blob_header():
     desc = lay.desc()
     assert meta.size == desc.meta_bytes and meta.size % 256 == 0
     assert int(meta[:4].view(np.uint32)[0]) == 0x564B5748
-    assert int(meta[4:8].view(np.uint32)[0]) == 1
+    assert int(meta[4:8].view(np.uint32)[0]) == hw.ABI_VERSION == hw.hwkv_abi_version()
     assert int(meta[8:16].view(np.uint64)[0]) == desc.fingerprint
+    assert hw.hwkv_meta_fingerprint(meta) == desc.fingerprint
+
+
+def test_meta_fingerprint_rejects_other_blobs():
+    lay = hw.hwkv_layout_create(CONFIG_WINDOWS["tiny"], 16, 64, "f32")
+    meta = hw.hwkv_meta_fill(lay)
+    with pytest.raises(hw.HwkvError) as e:
+        hw.hwkv_meta_fingerprint(meta[:32])
+    assert e.value.status_name == "HWKV_ERR_INVALID_ARG"
+    junk = meta.copy()
+    junk[:4] = 0
+    with pytest.raises(hw.HwkvError) as e:
+        hw.hwkv_meta_fingerprint(junk)
+    assert e.value.status_name == "HWKV_ERR_ABI_MISMATCH"
+    old = meta.copy()
+    old[4:8] = np.array([hw.ABI_VERSION - 1], np.uint32).view(np.uint8)
+    with pytest.raises(hw.HwkvError) as e:
+        hw.hwkv_meta_fingerprint(old)
+    assert e.value.status_name == "HWKV_ERR_ABI_MISMATCH"
+    assert "ABI version %d" % (hw.ABI_VERSION - 1) in str(e.value)
 
 
 def test_fingerprint_tracks_every_parameter():
@@ -243,9 +266,75 @@ def test_table_fill_overflow_is_reported():
     assert e.value.status_name == "HWKV_ERR_OVERFLOW"
 
 
-def _fake_cache(lay, pool_bytes, rows, pool_ptr=1 << 20):
+def _fake_cache(lay, pool_bytes, rows, pool_ptr=1 << 20, fingerprint=None):
     # device pointers are never dereferenced: validation fails first
-    return hw.hwkv_cache(pool_ptr, pool_bytes, 2 << 20, rows, 3 << 20)
+    fp = lay.desc().fingerprint if fingerprint is None else fingerprint
+    return hw.hwkv_cache(pool_ptr, pool_bytes, 2 << 20, rows, 3 << 20, fp)
+
+
+def _every_device_call(lay, cv, scale=0.1, n_q=4, with_scale_only=False):
+    """Status of every device entry point on cache view cv with fake device
+    pointers, in the order of the header.  Callers make sure that every call
+    fails validation: a call that passed would launch a kernel on them.
+    with_scale_only: only the attention calls (which take a scale)."""
+    P = lambda mib: ctypes.c_void_p(mib << 20)  # noqa: E731
+    L = hw._lib
+    h = lay.handle
+    c = ctypes.byref(cv)
+    big = 1 << 40
+    head = [] if with_scale_only else [
+        L.hwkv_append(h, c, 0, 1, 1, None, P(4), 1, P(5), P(6), None)]
+    mid = [] if with_scale_only else [
+        L.hwkv_decode_merge(h, c, 0, 1, 1, P(10), n_q, P(8), big, P(11), 0, None)]
+    return head + [
+        L.hwkv_decode_split(h, c, 0, 1, 1, None, P(10), n_q, P(9), scale, P(8), big, None),
+    ] + mid + [
+        L.hwkv_decode_attn(h, c, 0, 1, 1, None, P(10), n_q, P(9), scale, P(8), big, P(11), 0,
+                           None),
+        L.hwkv_decode_split_append(h, c, 0, 1, 1, None, P(10), P(5), P(6), n_q, P(9), scale, P(8),
+                                   big, None),
+        L.hwkv_decode_append_attn(h, c, 0, 1, 1, None, P(10), P(5), P(6), n_q, P(9), scale, P(8),
+                                  big, P(11), 0, None),
+        L.hwkv_decode_step(h, c, 0, 1, 1, None, P(10), P(5), P(6), n_q, P(9), scale, P(8), big,
+                           P(11), 0, None),
+        L.hwkv_prefill_attn(h, c, 0, 1, None, P(10), 7, n_q, P(9), P(5), P(6), P(11), 0, scale,
+                            None),
+        L.hwkv_prefill_attn_exact(h, c, 0, 1, None, P(10), 7, n_q, P(9), P(5), P(6), P(11), 0,
+                                  scale, None),
+    ]
+
+
+def test_cache_of_another_layout_is_rejected_before_launch():
+    """Kernel-ABI check (page "KV Cache Management in Hybrid Attention LLMs",
+    4.2): a cache view whose blob was written for another layout (here one
+    window differs by one token) is refused by every device call, on the host,
+    before anything is enqueued."""
+    a = hw.hwkv_layout_create([[32, 128]], 16, 64, "bf16")
+    b = hw.hwkv_layout_create([[32, 129]], 16, 64, "bf16")
+    fa, fb = a.desc().fingerprint, b.desc().fingerprint
+    assert fa != fb
+    cv = _fake_cache(b, hw.hwkv_mem_estimate(b, 1), 1, fingerprint=fa)
+    got = _every_device_call(b, cv)
+    assert [hw.STATUS_NAMES[s] for s in got] == ["HWKV_ERR_ABI_MISMATCH"] * len(got)
+    msg = hw.hwkv_last_error()
+    assert "%016x" % fa in msg and "%016x" % fb in msg
+    # the blob's own fingerprint, read back from a host copy, is what a
+    # caller puts in the view; the same calls then get past this check and
+    # stop at the next one (a pool one byte short of the estimate)
+    cv_ok = _fake_cache(b, hw.hwkv_mem_estimate(b, 1) - 1, 1,
+                        fingerprint=hw.hwkv_meta_fingerprint(hw.hwkv_meta_fill(b)))
+    got = _every_device_call(b, cv_ok)
+    assert [hw.STATUS_NAMES[s] for s in got] == ["HWKV_ERR_CAPACITY"] * len(got)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.125, float("nan"), float("inf"),
+                                   float("-inf")])
+def test_non_positive_or_non_finite_scale_is_rejected(scale):
+    lay = hw.hwkv_layout_create([[32, 128]], 16, 64, "bf16")
+    cv = _fake_cache(lay, hw.hwkv_mem_estimate(lay, 1), 1)
+    got = _every_device_call(lay, cv, scale=scale, with_scale_only=True)
+    assert [hw.STATUS_NAMES[s] for s in got] == ["HWKV_ERR_INVALID_ARG"] * 7
+    assert "scale must be finite and > 0" in hw.hwkv_last_error()
 
 
 def test_capacity_error_names_layer_and_head():

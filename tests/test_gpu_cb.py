@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import synth
-from _gpu_common import BF16_TOL, device, hw, row_rel_err, say
+from _gpu_common import BF16_TOL, DECODE_REGRESSION_TOL, device, hw, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +117,4 @@ def test_continuous_batch_sampled():
             worst = max(worst, row_rel_err(got, ref[0, 0]))
     say("cb: max row rel err", worst)
     assert worst <= BF16_TOL
+    assert worst <= DECODE_REGRESSION_TOL, worst

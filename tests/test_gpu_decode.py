@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import synth
-from _gpu_common import (BF16_TOL, F32_TOL, bf16_round, bf16_ulps_apart, build_decode_case,
-                         build_stack_case, device, f16_ulps_apart, hw, oracle_decode, row_rel_err,
+from _gpu_common import (BF16_TOL, DECODE_REGRESSION_TOL, F32_TOL, bf16_round, bf16_ulps_apart,
+                         build_decode_case, build_stack_case, device, f16_ulps_apart, hw, oracle_decode, row_rel_err,
                          run_decode_step, say, stack_oracle_layer, stack_step, to_host_f64)
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +30,7 @@ def _check(case, out, **kw):
     err = row_rel_err(got, ref)
     say("max row rel err", err)
     assert err <= _tol(case.dtype), err
+    assert err <= DECODE_REGRESSION_TOL, err
     return got, ref
 
 
@@ -200,6 +201,7 @@ def test_single_layer_config():
     err = row_rel_err(to_host_f64(out[0:1]), ref)
     say("single-layer max row rel err", err)
     assert err <= BF16_TOL
+    assert err <= DECODE_REGRESSION_TOL, err
 
 
 def test_stack48_config():
@@ -218,3 +220,4 @@ def test_stack48_config():
         worst = max(worst, row_rel_err(got[l:l + 1], ref))
     say("stack48 max row rel err", worst)
     assert worst <= BF16_TOL
+    assert worst <= DECODE_REGRESSION_TOL, worst

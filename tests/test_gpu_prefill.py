@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import synth
-from _gpu_common import BF16_TOL, device, hw, row_rel_err, say, to_host_f64
+from _gpu_common import (BF16_TOL, DECODE_REGRESSION_TOL, device, hw, row_rel_err, say,
+                         to_host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +135,18 @@ def test_f16_output():
     assert np.abs(got - ref16).max() <= np.abs(ref).max() * 2 ** -10
 
 
+def test_f16_output_default_entry():
+    """The default entry (P in fp16 for the P.V product) with fp16 outputs,
+    against the oracle at the gate: the fp16-P error (3-4.5e-4 of the row
+    maximum, measured) plus the output rounding (at most half a binary16 ulp,
+    2^-11 of the row maximum) stay well inside 2e-3."""
+    say("prefill f16 out, default entry")
+    c = PrefillCase([64, 130, 2000], 128, 2, [500, 0], 100, seed=409)
+    _check(to_host_f64(c.run(out_dtype=torch.float16)), c.oracle())
+    c16 = PrefillCase([64, 130, 2000], 128, 2, [500, 0], 100, seed=410, dtype=torch.float16)
+    _check(to_host_f64(c16.run(out_dtype=torch.float16)), c16.oracle())
+
+
 def test_chunk_size_invariance_and_last_row_equals_decode():
     """Prefill n rows at once == prefill n1, append n1, prefill the rest; the
     last row equals a decode step at L = P + n after appending the chunk.
@@ -175,12 +188,18 @@ def test_chunk_size_invariance_and_last_row_equals_decode():
     assert row_rel_err(to_host_f64(dec[0, 0]), to_host_f64(o_all[0, n - 1])) <= 1e-5
 
 
-def test_prefill_config_161k_sampled_rows():
+def test_prefill_config_161k_then_append_and_decode():
     """4 sequences at 161K context, one 2048-token chunk, windows of the
     printed policy's layer 0 (up to 65536): sampled rows (first, last, tile
-    and window edges, random) of every head against the oracle."""
+    and window edges, random) of every head against the oracle; then the
+    chunk is appended and decode steps follow (the appending split, two
+    launches per step), every head checked against the oracle over the
+    logical stream history + chunk + new tokens."""
+    H = hw()
+    dev = device()
+    P, n, n_kv, G, d = synth.CTX_161K, 2048, 8, 3, 128
     say("prefill 161K config: fill")
-    c = PrefillCase(list(synth.YAML_LAYER0), 128, 3, [synth.CTX_161K] * 4, 2048, seed=105)
+    c = PrefillCase(list(synth.YAML_LAYER0), d, G, [P] * 4, n, seed=105)
     say("prefill 161K config: run")
     got = to_host_f64(c.run())
     rng = np.random.default_rng(7)
@@ -189,6 +208,41 @@ def test_prefill_config_161k_sampled_rows():
     say("prefill 161K config: oracle on", len(rows), "rows")
     ref = c.oracle(rows=rows)
     _check(got[:, rows], ref)
+
+    say("prefill 161K config: append the chunk, decode")
+    pos0 = torch.tensor(c.pos0, device=dev)
+    H.hwkv_append(c.cache, 0, 1, pos0, c.k[None], c.v[None])
+    steps = 3
+    g = synth.gen(1051, dev)
+    kd = synth.randn((steps, 1, 4, 1, n_kv, d), torch.bfloat16, g)
+    vd = synth.randn((steps, 1, 4, 1, n_kv, d), torch.bfloat16, g)
+    qd = synth.randn((steps, 1, 4, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+    ws = H.make_workspace(c.lay, 0, 1, 4, n_kv * G, device=dev)
+    outs = []
+    for i in range(steps):
+        out = torch.full((1, 4, n_kv * G, d), float("nan"), dtype=torch.float32, device=dev)
+        H.hwkv_decode_append_attn(c.cache, 0, 1, pos0 + n + i, kd[i], vd[i], qd[i],
+                                  1.0 / math.sqrt(d), ws, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    # logical stream of every sequence from the history base on
+    k_all = np.concatenate([c.k_hist, synth.to_raw(c.k), synth.to_raw(kd[:, 0, :, 0]
+                                                                      ).transpose(1, 0, 2, 3)],
+                           axis=1)[None]
+    v_all = np.concatenate([c.v_hist, synth.to_raw(c.v), synth.to_raw(vd[:, 0, :, 0]
+                                                                      ).transpose(1, 0, 2, 3)],
+                           axis=1)[None]
+    worst = 0.0
+    for i in range(steps):
+        L = P + n + i + 1
+        ref = oracle.decode(c.windows[None, :], [L] * 4, synth.to_raw(qd[i]), k_all, v_all,
+                            c.hbase, 1.0 / math.sqrt(d))
+        o = to_host_f64(outs[i])
+        assert np.all(np.isfinite(o))
+        worst = max(worst, row_rel_err(o, ref))
+    say("161K decode after prefill: max row rel err", worst)
+    assert worst <= BF16_TOL
+    assert worst <= DECODE_REGRESSION_TOL, worst
 
 
 @pytest.mark.parametrize("d,G", [(128, 3), (64, 2), (128, 8)])

@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import synth
-from _gpu_common import (BF16_TOL, F32_TOL, build_decode_case, build_stack_case, device, hw,
-                         oracle_decode, row_rel_err, run_decode_step, say, stack_oracle_layer,
+from _gpu_common import (BF16_TOL, DECODE_REGRESSION_TOL, F32_TOL, build_decode_case,
+                         build_stack_case, device, hw, oracle_decode, row_rel_err, run_decode_step, say, stack_oracle_layer,
                          stack_step, to_host_f64)
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +75,7 @@ def test_step_equals_append_then_attn(case, two_launch):
     err = row_rel_err(to_host_f64(o_f), ref)
     say("fused max row rel err", err)
     assert err <= (BF16_TOL if dtype == torch.bfloat16 else F32_TOL)
+    assert err <= DECODE_REGRESSION_TOL, err
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
@@ -272,6 +273,7 @@ def test_stack48_step_full_size():
         worst = max(worst, row_rel_err(got[l:l + 1], stack_oracle_layer(f, l)))
     say("stack48 fused max row rel err (sampled layers)", worst)
     assert worst <= BF16_TOL
+    assert worst <= DECODE_REGRESSION_TOL, worst
 
 
 def test_stack48_per_layer_split384():
@@ -301,3 +303,4 @@ def test_stack48_per_layer_split384():
         worst = max(worst, row_rel_err(got[l:l + 1], stack_oracle_layer(c, l)))
     say("stack48 per layer split 384 max row rel err (sampled layers)", worst)
     assert worst <= BF16_TOL
+    assert worst <= DECODE_REGRESSION_TOL, worst
