@@ -41,7 +41,7 @@ EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_l
             "hwkv_meta_fill", "hwkv_meta_fingerprint",
             "hwkv_workspace_bytes", "hwkv_append", "hwkv_decode_split", "hwkv_decode_merge",
             "hwkv_decode_attn", "hwkv_decode_split_append", "hwkv_decode_append_attn",
-            "hwkv_step_workspace_bytes",
+            "hwkv_decode_append_attn_static", "hwkv_step_workspace_bytes",
             "hwkv_decode_step",
             "hwkv_prefill_attn", "hwkv_prefill_attn_exact")
 
@@ -106,6 +106,12 @@ _lib.hwkv_decode_split_append.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32,
 _lib.hwkv_decode_append_attn.restype = ctypes.c_int
 _lib.hwkv_decode_append_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _vp,
                                          _vp, _i32, _vp, _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
+_lib.hwkv_decode_append_attn_static.restype = ctypes.c_int
+_lib.hwkv_decode_append_attn_static.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp,
+                                                _vp, _vp, _i32, _vp, _f32, _vp, ctypes.c_int,
+                                                _vp]
+#: bytes of the library's static decode scratch (hwkv_decode_append_attn_static)
+STATIC_SCRATCH_BYTES = 64 << 20
 _lib.hwkv_step_workspace_bytes.restype = ctypes.c_int
 _lib.hwkv_step_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _i32, _P(_u64)]
 _lib.hwkv_decode_step.restype = ctypes.c_int
@@ -473,6 +479,32 @@ def hwkv_decode_append_attn(cache: Cache, layer_begin: int, n_layers: int, pos: 
     q, out: [n_layers][n_seqs][n_q_heads][head_dim]; workspace: make_workspace."""
     _decode_with_append(_lib.hwkv_decode_append_attn, cache, layer_begin, n_layers, pos, k_new,
                         v_new, q, scale, workspace, out, seq_slots, stream)
+
+
+def hwkv_decode_append_attn_static(cache: Cache, layer_begin: int, n_layers: int,
+                                   pos: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                   q: torch.Tensor, scale: float, out: torch.Tensor,
+                                   seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """hwkv_decode_append_attn with the split records in the library's static
+    scratch (no workspace argument; the call allocates nothing)."""
+    d = cache.layout.desc()
+    n_seqs, n_q = int(q.shape[1]), int(q.shape[2])
+    _expect("q", q, (n_layers, n_seqs, n_q, d.head_dim), torch_dtype(d.dtype))
+    kv_shape = (n_layers, n_seqs, d.n_kv_heads, d.head_dim)
+    if k_new.dim() == 5:
+        kv_shape = (n_layers, n_seqs, 1, d.n_kv_heads, d.head_dim)
+    _expect("k_new", k_new, kv_shape, torch_dtype(d.dtype))
+    _expect("v_new", v_new, kv_shape, torch_dtype(d.dtype))
+    if out.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError("out must be float32, bfloat16 or float16")
+    _expect("out", out, tuple(q.shape), out.dtype)
+    _expect("pos", pos, (n_seqs,), torch.int64)
+    _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
+    cv = cache.view()
+    _check(_lib.hwkv_decode_append_attn_static(
+        cache.layout.handle, ctypes.byref(cv), layer_begin, n_layers, n_seqs, _ptr(seq_slots),
+        _ptr(pos), _ptr(k_new), _ptr(v_new), n_q, _ptr(q), scale, _ptr(out),
+        _dtype_code(out.dtype), _stream(stream)))
 
 
 def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.Tensor,

@@ -339,6 +339,29 @@ hwkv_status hwkv_decode_append_attn(const hwkv_layout* L, const hwkv_cache* c,
                               n_q_heads, q, scale, ws, ws_bytes, out, out_dtype, stream);
 }
 
+hwkv_status hwkv_decode_append_attn_static(const hwkv_layout* L, const hwkv_cache* c,
+                                           int32_t layer_begin, int32_t n_layers,
+                                           int32_t n_seqs, const int32_t* seq_slots,
+                                           const int64_t* pos, const void* k_new,
+                                           const void* v_new, int32_t n_q_heads, const void* q,
+                                           float scale, void* out, hwkv_dtype out_dtype,
+                                           hipStream_t stream) {
+    clear_error();
+    uint64_t need = 0;
+    HWKV_TRY(hwkv_workspace_bytes(L, layer_begin, n_layers, n_seqs, n_q_heads, &need));
+    if (need > HWKV_STATIC_SCRATCH_BYTES)
+        return fail(HWKV_ERR_CAPACITY,
+                    "this call needs " + std::to_string(need) + " bytes of split records; the "
+                    "static scratch holds " + std::to_string(HWKV_STATIC_SCRATCH_BYTES) +
+                    " (fewer layers or sequences per call, or hwkv_decode_append_attn with a "
+                    "caller workspace)");
+    void* ws = nullptr;
+    HWKV_TRY(static_scratch(stream, &ws));
+    return decode_append_attn(L, c, layer_begin, n_layers, n_seqs, seq_slots, pos, k_new, v_new,
+                              n_q_heads, q, scale, ws, HWKV_STATIC_SCRATCH_BYTES, out, out_dtype,
+                              stream);
+}
+
 hwkv_status hwkv_decode_step(const hwkv_layout* L, const hwkv_cache* c, int32_t layer_begin,
                              int32_t n_layers, int32_t n_seqs, const int32_t* seq_slots,
                              const int64_t* pos, const void* k_new, const void* v_new,

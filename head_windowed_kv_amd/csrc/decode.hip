@@ -31,11 +31,59 @@
 // exponential is one v_exp_f32.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "hwkv_internal.h"
 
+// Split records of hwkv_decode_append_attn_static, for callers that cannot
+// allocate device memory.  Every device the library runs on holds one copy
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for that device (the name is a host-side
+// stand-in there).
+static __device__ __align__(256) uint8_t scratch[HWKV_STATIC_SCRATCH_BYTES];
+
 namespace hwkv {
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];  // per device, looked up once
+}  // namespace
+
+hwkv_status static_scratch(hipStream_t stream, void** ptr) {
+    int cur = -1, dev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) {
+        dev = cur;
+        if (stream) e = hipStreamGetDevice(stream, &dev);  // the stream's device
+    }
+    if (e != hipSuccess)
+        return fail(HWKV_ERR_HIP, std::string("static scratch: device query: ") +
+                                      hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(HWKV_ERR_UNSUPPORTED, "static scratch: device index " + std::to_string(dev) +
+                                              " beyond " + std::to_string(kMaxScratchDevices));
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        // the symbol's address on `dev`, looked up with that device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(HWKV_ERR_HIP, std::string("static scratch: ") + hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess || !p)
+            return fail(HWKV_ERR_HIP, std::string("static scratch: hipGetSymbolAddress: ") +
+                                          hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return HWKV_OK;
+}
+
 namespace {
 
 // The kernels walk every head's window in tiles of kBS = 16 tokens.  A cache

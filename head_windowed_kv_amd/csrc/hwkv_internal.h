@@ -202,6 +202,12 @@ struct PrefillArgs {
     float qk_scale_log2;
 };
 
+// Device address of the library's static decode scratch (the records of
+// hwkv_decode_append_attn_static) on the device that `stream` runs on: a
+// file-scope array of HWKV_STATIC_SCRATCH_BYTES in decode.hip, looked up once
+// per device with hipGetSymbolAddress and kept.
+hwkv_status static_scratch(hipStream_t stream, void** ptr);
+
 hwkv_status launch_append(const hwkv_layout& lay, const AppendArgs& a, hipStream_t s);
 hwkv_status launch_decode_split(const hwkv_layout& lay, int group, const DecodeSplitArgs& a,
                                 hipStream_t s);

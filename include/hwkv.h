@@ -324,6 +324,28 @@ hwkv_status hwkv_decode_append_attn(const hwkv_layout *layout, const hwkv_cache 
                                     void *workspace, uint64_t workspace_bytes, void *out,
                                     hwkv_dtype out_dtype, hipStream_t stream);
 
+/* hwkv_decode_append_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches and the same results bit for bit, with the
+ * split records in a scratch array of HWKV_STATIC_SCRATCH_BYTES that the
+ * library keeps on every device it runs on until the process ends, instead
+ * of a caller workspace.  The call allocates nothing; the first call on a
+ * device looks the array's address up (make it outside graph capture).
+ * HWKV_ERR_CAPACITY when hwkv_workspace_bytes of the call exceeds the array
+ * (e.g. the 48-layer 112K stack fits up to 5 sequences per call at the
+ * default split).  All calls on one device share its array: two such calls
+ * that overlap in time on one device (different streams) race; calls on one
+ * stream are ordered and safe. */
+#define HWKV_STATIC_SCRATCH_BYTES (64ull << 20)
+hwkv_status hwkv_decode_append_attn_static(const hwkv_layout *layout,
+                                           const hwkv_cache *cache, int32_t layer_begin,
+                                           int32_t n_layers, int32_t n_seqs,
+                                           const int32_t *seq_slots, const int64_t *pos,
+                                           const void *k_new, const void *v_new,
+                                           int32_t n_q_heads, const void *q, float scale,
+                                           void *out, hwkv_dtype out_dtype,
+                                           hipStream_t stream);
+
 /* Device workspace of hwkv_decode_step: the hwkv_workspace_bytes records,
  * padded to 256 bytes, then one uint32 arrival counter per (layer, kv head,
  * sequence).  The counters must be zero before the first hwkv_decode_step on

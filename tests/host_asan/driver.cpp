@@ -122,6 +122,9 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
                                    HWKV_F16, nullptr) == HWKV_OK);
     EXPECT(hwkv_decode_step(lay, &c, 0, L, ns, slots, pos, k, v, nq, q, 0.1f, wsp, sws, out,
                             HWKV_F32, nullptr) == HWKV_OK);
+    if (ws <= HWKV_STATIC_SCRATCH_BYTES)
+        EXPECT(hwkv_decode_append_attn_static(lay, &c, 0, L, ns, slots, pos, k, v, nq, q, 0.1f,
+                                              out, HWKV_BF16, nullptr) == HWKV_OK);
     EXPECT(hwkv_prefill_attn(lay, &c, L - 1, ns, slots, pos, 77, nq, q, k, v, out, HWKV_BF16,
                              0.1f, nullptr) == HWKV_OK);
     EXPECT(hwkv_prefill_attn_exact(lay, &c, 0, ns, nullptr, pos, 1, nq, q, k, v, out, HWKV_F32,
@@ -155,6 +158,10 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
                                    0.1f, nullptr) != HWKV_OK);
     EXPECT(hwkv_prefill_attn(lay, nullptr, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, 0.1f,
                              nullptr) != HWKV_OK);
+    // the static scratch refuses a call whose records exceed it
+    EXPECT(hwkv_decode_append_attn_static(lay, &c, 0, L, 65535, slots, pos, k, v, nq, q, 0.1f,
+                                          out, HWKV_F32, nullptr) == HWKV_ERR_CAPACITY);
+    EXPECT(strstr(hwkv_last_error(), "static scratch") != nullptr);
     // a view whose blob belongs to another layout (kernel-ABI check)
     hwkv_cache other = c;
     other.meta_fingerprint ^= 1;

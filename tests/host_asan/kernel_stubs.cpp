@@ -8,6 +8,12 @@ namespace hwkv {
 
 int g_launches = 0;
 
+// a fake, suitably aligned device address for the static scratch
+hwkv_status static_scratch(hipStream_t, void** ptr) {
+    *ptr = reinterpret_cast<void*>(uintptr_t(7) << 30);
+    return HWKV_OK;
+}
+
 bool append_supported(const hwkv_layout&) { return true; }
 bool decode_supported(const hwkv_layout&, int) { return true; }
 bool prefill_supported(const hwkv_layout&, int) { return true; }

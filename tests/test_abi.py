@@ -392,3 +392,22 @@ def test_decode_argument_errors_before_launch():
     # non-finite scale
     assert f(lay.handle, ctypes.byref(cv), 0, 1, 1, None, ctx, 4, q, float("inf"), ws, need, out,
              0, None) == 1
+
+
+def test_static_scratch_entry_refuses_calls_beyond_its_array():
+    """hwkv_decode_append_attn_static (callers that cannot allocate) keeps its
+    split records in a static array of HWKV_STATIC_SCRATCH_BYTES: the 48-layer
+    112K stack fits 5 sequences per call; 6 are refused on the host, before
+    any device is touched."""
+    text = open(os.path.join(ROOT, "include", "hwkv.h")).read()
+    m = re.search(r"#define HWKV_STATIC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == hw.STATIC_SCRATCH_BYTES
+    lay = hw.hwkv_layout_create(CONFIG_WINDOWS["stack48"], 16, 128, "bf16")
+    assert hw.hwkv_workspace_bytes(lay, 0, 48, 5, 24) <= hw.STATIC_SCRATCH_BYTES
+    assert hw.hwkv_workspace_bytes(lay, 0, 48, 6, 24) > hw.STATIC_SCRATCH_BYTES
+    cv = _fake_cache(lay, hw.hwkv_mem_estimate(lay, 6), 6)
+    P = lambda mib: ctypes.c_void_p(mib << 20)  # noqa: E731
+    st = hw._lib.hwkv_decode_append_attn_static(lay.handle, ctypes.byref(cv), 0, 48, 6, None,
+                                                P(10), P(5), P(6), 24, P(9), 0.1, P(11), 0, None)
+    assert hw.STATUS_NAMES[st] == "HWKV_ERR_CAPACITY"
+    assert "static scratch holds %d" % hw.STATIC_SCRATCH_BYTES in hw.hwkv_last_error()
