@@ -53,6 +53,8 @@ def parse():
                    help="stack48: the 48-layer 112K decode step (default, the headline line); "
                         "cb: the 32-sequence continuous batch, 256 steps (138 GB pool)")
     p.add_argument("--cb-steps", type=int, default=256)
+    p.add_argument("--no-cb", action="store_true",
+                   help="skip the continuous-batch leg of the default run")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--counter-pass", action="store_true",
@@ -246,7 +248,9 @@ def main():
     torch.cuda.synchronize()
     t_fill = time.time() - t_fill
 
-    n_steps = args.warmup + args.steps
+    # warmup steps, the timed steps, then as many again for the split-kernel
+    # timing pass (the token stream continues through all of them)
+    n_steps = args.warmup + 2 * args.steps
     g = synth.gen(104, dev)
     q = synth.randn((n_layers, n_seqs, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
     k_new = synth.randn((n_steps, n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
@@ -278,6 +282,10 @@ def main():
             evp[1].record(stream)
         H.hwkv_decode_merge(cache, 0, n_layers, ctx[i], ws, out, stream=stream)
 
+    # the practical read ceiling (a plain streaming read over the same pool)
+    # is measured first: it also brings the GPU to its steady clocks before
+    # the warmup steps
+    ceiling = read_ceiling(torch, cache.pool)
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
@@ -287,15 +295,21 @@ def main():
         probe_copy_once(torch, dev)
         print(json.dumps({"counter_pass": True, "steps": args.steps}), flush=True)
         return
+    # the timed region: K consecutive steps, nothing recorded between them
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for j in range(args.steps):
-        run_step(args.warmup + j, ev[j])
+        run_step(args.warmup + j)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
+    # the split kernel's own duration, from a separate pass of K more steps
+    # with HIP events around each split launch on the stream it runs on
+    for j in range(args.steps):
+        run_step(args.warmup + args.steps + j, ev[j])
+    torch.cuda.synchronize()
     split_ms = [a.elapsed_time(b) for a, b in ev]
     split_avg_ms = sum(split_ms) / len(split_ms)
     bytes_step = step_bytes(L0 + args.warmup + 1)
@@ -337,18 +351,26 @@ def main():
             "unit": "GB/s",
             "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(desc.split_tokens),
+            "traffic_source": "committed rocprofv3 --pmc counters (FETCH_SIZE, WRITE_SIZE per "
+                              "dispatch, scaled by the probe copy of known size) in "
+                              "profiles/decode_split_stack48_counters.json; reported only while "
+                              "the kernel source hash and split length match (else null)",
             "avg_launch_ms": round(split_avg_ms, 4),
+            "avg_launch_timing": "HIP events around each split launch, in a pass of %d steps "
+                                 "after the timed region" % args.steps,
             "algorithmic_bytes_per_launch": bytes_step,
         },
         "fill_seconds": round(t_fill, 2),
     }
-    ceiling = read_ceiling(torch, cache.pool)
     result["practical_read_ceiling_gbps"] = round(ceiling, 1)
     result["roofline"]["frac_of_practical_ceiling"] = round(split_gbps / ceiling, 4)
 
     result["three_launch_step"] = three_launch_leg(H, torch, cache, q, k_new, v_new,
                                                    L0 + n_steps, n_seqs, args.steps, step_bytes,
                                                    scale, ws, out)
+    result["two_launch_step_repeat"] = fused_leg(H, torch, cache, lay, q, k_new, v_new,
+                                                 L0 + n_steps + 16, n_seqs, n_kv, G, d,
+                                                 args.steps, step_bytes, two_launch=True)
     result["single_launch_step"] = fused_leg(H, torch, cache, lay, q, k_new, v_new,
                                              L0 + n_steps + 32, n_seqs, n_kv, G, d, args.steps,
                                              step_bytes)
@@ -367,22 +389,42 @@ def main():
         result["prefill_161k"] = prefill_leg(H, torch, synth)
         torch.cuda.empty_cache()
         result["single_layer_8seqs_ctx32k"] = single_layer_leg(H, torch, synth)
+    if not args.no_cb:
+        torch.cuda.empty_cache()
+        result["continuous_batch_32seq"] = cb_leg(args, H, torch, synth)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(windows, L0, n_kv, G, d, args.cpu_seconds,
-                                              tok_per_s)
+                                              tok_per_s, result.get("prefill_161k"))
     print(json.dumps(result), flush=True)
 
 
 def cb_run(args):
-    """Continuous batch: 32 sequences with contexts uniform in [4K, 160K],
-    the 48-layer stack's windows, 256 decode steps of append + attention,
-    one launch of each kernel per step for all layers and sequences."""
-    import numpy as np
+    """`--config cb`: the continuous batch as the JSON line itself."""
     import torch
 
     import head_windowed_kv_amd as H
     import synth
+    torch.cuda.set_device(0)
+    leg = cb_leg(args, H, torch, synth)
+    res = {"metric": METRIC, "value": leg["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": leg["steps"], "warmup": 2, "ms_per_step": leg["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": leg["config"],
+           "kv_read_gbps": leg["kv_read_gbps"], "kv_read_frac_of_peak": leg["kv_read_frac_of_peak"],
+           "roofline": leg["roofline"], "fill_seconds": leg["fill_seconds"]}
+    print(json.dumps(res), flush=True)
+
+
+def cb_leg(args, H, torch, synth):
+    """Continuous batch: 32 sequences with contexts uniform in [4K, 160K],
+    the 48-layer stack's windows, 256 decode steps of append + attention
+    (hwkv_decode_append_attn: the split stage appends each sequence's new
+    token, then the merge), one launch of each kernel per step for all
+    layers and sequences.  Then a pass of 16 more steps with HIP events
+    around each split launch gives the split kernel's roofline."""
+    import numpy as np
 
     dev = torch.device("cuda", 0)
     n_layers, n_kv, G, d = 48, 8, 3, 128
@@ -392,6 +434,7 @@ def cb_run(args):
     lay = H.hwkv_layout_create(windows, 16, d, torch.bfloat16, args.split_tokens)
     t = time.time()
     cache = H.make_cache(lay, n_seqs, device=dev)
+    pool_bytes = cache.pool.numel()
     synth.fill_normal(cache.pool, 104, progress=True)
     torch.cuda.synchronize()
     t_fill = time.time() - t
@@ -403,8 +446,9 @@ def cb_run(args):
     n_steps = args.cb_steps
     kn = synth.randn((n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
     vn = synth.randn((n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
-    pos = [L0_t + i for i in range(n_steps + 2)]
-    ctx = [L0_t + i + 1 for i in range(n_steps + 2)]
+    n_roof = 16
+    pos = [L0_t + i for i in range(n_steps + 2 + n_roof)]
+    ctx = [p + 1 for p in pos]
     scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream()
 
@@ -422,22 +466,47 @@ def cb_run(args):
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     w64 = windows.astype(np.int64).reshape(-1)
-    kv_bytes = sum(float(np.minimum(w64[None, :], (L0 + 3 + i)[:, None]).sum())
-                   for i in range(n_steps)) * KV_BYTES_PER_TOK_HEAD
-    res = {"metric": METRIC, "value": round(n_seqs * n_steps / (total_ms / 1e3), 2),
-           "unit": "tokens/s", "n_gpus": 1, "steps": n_steps, "warmup": 2,
-           "ms_per_step": round(total_ms / n_steps, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "continuous_batch_32seq_ctx4k_160k_stack48",
-                      "layers": n_layers, "kv_heads": n_kv, "q_heads": n_kv * G, "head_dim": d,
-                      "block_size": 16, "batch": n_seqs,
-                      "contexts": "uniform integers in [4096, 163840], numpy default_rng(1)",
-                      "split_tokens": lay.desc().split_tokens,
-                      "pool_bytes": cache.pool.numel()},
-           "kv_read_gbps": round(kv_bytes / (total_ms / 1e3) / 1e9, 1),
-           "kv_read_frac_of_peak": round(kv_bytes / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-           "fill_seconds": round(t_fill, 1)}
-    print(json.dumps(res), flush=True)
+
+    def bytes_at(L):  # K/V bytes every head of every sequence reads at contexts L
+        return float(np.minimum(w64[None, :], np.asarray(L)[:, None]).sum()) * \
+            KV_BYTES_PER_TOK_HEAD
+    kv_bytes = sum(bytes_at(L0 + 3 + i) for i in range(n_steps))
+    # split-kernel pass: the two stage calls of the same step, events around the split
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_roof)]
+    roof_bytes = 0.0
+    for j in range(n_roof):
+        i = 2 + n_steps + j
+        ev[j][0].record(s)
+        H.hwkv_decode_split_append(cache, 0, n_layers, pos[i], kn, vn, q, scale, ws)
+        ev[j][1].record(s)
+        H.hwkv_decode_merge(cache, 0, n_layers, ctx[i], ws, out)
+        roof_bytes += bytes_at(L0 + i + 1)
+    torch.cuda.synchronize()
+    split_ms = sum(a.elapsed_time(b) for a, b in ev) / n_roof
+    split_gbps = roof_bytes / n_roof / (split_ms / 1e3) / 1e9
+    del cache
+    return {"workload": "continuous_batch_32seq_ctx4k_160k_stack48",
+            "config": {"workload": "continuous_batch_32seq_ctx4k_160k_stack48",
+                       "layers": n_layers, "kv_heads": n_kv, "q_heads": n_kv * G,
+                       "head_dim": d, "block_size": 16, "batch": n_seqs,
+                       "contexts": "uniform integers in [4096, 163840], numpy default_rng(1)",
+                       "split_tokens": lay.desc().split_tokens, "pool_bytes": pool_bytes},
+            "steps": n_steps, "ms_per_step": round(total_ms / n_steps, 4),
+            "tokens_per_s": round(n_seqs * n_steps / (total_ms / 1e3), 2),
+            "kv_read_bytes_total": kv_bytes,
+            "kv_read_gbps": round(kv_bytes / (total_ms / 1e3) / 1e9, 1),
+            "kv_read_frac_of_peak": round(kv_bytes / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "launch": "hwkv_decode_append_attn per step: appending split + merge for all 48 "
+                      "layers and 32 sequences",
+            "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16, d128, G3, append>",
+                         "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "avg_launch_ms": round(split_ms, 4),
+                         "algorithmic_bytes_per_launch": roof_bytes / n_roof,
+                         "avg_launch_timing": "HIP events around each split launch, %d steps "
+                                              "after the timed ones" % n_roof},
+            "fill_seconds": round(t_fill, 1)}
 
 
 def gemm_reference_tflops(torch, n=16384, reps=5):
@@ -530,13 +599,11 @@ def prefill_leg(H, torch, synth):
                      std=1.0 / math.sqrt(d))
     posd = [torch.full((n_seqs,), P + n + i, dtype=torch.int64, device=dev)
             for i in range(n_warm + n_dec)]
-    ctxd = [p + 1 for p in posd]
     ws = H.make_workspace(lay, 0, 1, n_seqs, n_kv * G, device=dev)
     od = torch.empty((1, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
 
-    def dec_step(i):
-        H.hwkv_append(cache, 0, 1, posd[i], kd[i], vd[i])
-        H.hwkv_decode_attn(cache, 0, 1, ctxd[i], qd[i], scale, ws, od)
+    def dec_step(i):  # the appending split (it writes the new token) + the merge
+        H.hwkv_decode_append_attn(cache, 0, 1, posd[i], kd[i], vd[i], qd[i], scale, ws, od)
     for i in range(n_warm):
         dec_step(i)
     torch.cuda.synchronize()
@@ -567,7 +634,8 @@ def prefill_leg(H, torch, synth):
             "decode_step_ms": round(dec_ms, 4),
             "decode_tokens_per_s": round(n_seqs / (dec_ms / 1e3), 1),
             "decode_kv_read_gbps": round(dec_bytes / (dec_ms / 1e3) / 1e9, 1),
-            "decode_steps": n_dec}
+            "decode_steps": n_dec,
+            "decode_launch": "hwkv_decode_append_attn: appending split + merge per step"}
 
 
 def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n_kv, G, d,
@@ -756,11 +824,31 @@ def fused_leg(H, torch, cache, lay, q, k_new, v_new, L, n_seqs, n_kv, G, d, step
             "launches_per_step": 2 if two_launch else 1, "steps": steps}
 
 
-def cpu_baseline(windows, L, n_kv, G, d, target_s, gpu_tok_s):
-    """The fp64 oracle, as it is, on the host cores: one decode step of the
-    whole 48-layer stack, each layer's oracle call repeated until the layers
-    together have taken about target_s of CPU time (a full step takes ~1.6 s
-    on 16 cores); the step time is the sum over layers of the mean call time."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(windows, L, n_kv, G, d, target_s, gpu_tok_s, gpu_prefill=None):
+    """The fp64 oracle, as it is, on the host cores.
+
+    - All threads: one decode step of the whole 48-layer stack, each layer's
+      oracle call repeated until the layers together have taken about
+      target_s; the step time is the sum over layers of the mean call time.
+    - One thread: the same calls, layer by layer until ~target_s / 2 has
+      passed, the step time extrapolated by K/V bytes (labelled).
+    - The 161K chunked prefill: 16 evenly spaced chunk rows of each
+      (sequence, kv head) on all threads, extrapolated by the row count to
+      the 2048-row chunk (labelled).
+    - The continuous batch: the all-thread step time scaled by the batch's
+      K/V bytes per step (labelled)."""
     import numpy as np
     import torch
 
@@ -769,34 +857,105 @@ def cpu_baseline(windows, L, n_kv, G, d, target_s, gpu_tok_s):
 
     n_layers = windows.shape[0]
     threads = oracle.threads()
-    spent = 0.0
-    step_s = 0.0
-    calls = 0
     total_bytes = float(np.minimum(windows.astype(np.int64), L).sum()) * KV_BYTES_PER_TOK_HEAD
+    layer_bytes = np.minimum(windows.astype(np.int64), L).sum(axis=1) * KV_BYTES_PER_TOK_HEAD
+    inputs = {}
+
+    def layer_inputs(l):
+        if l not in inputs:
+            W = int(windows[l].max())
+            g = synth.gen(9000 + l)
+            q = synth.randn((1, 1, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+            k = synth.randn((1, 1, W, n_kv, d), torch.bfloat16, g)
+            v = synth.randn((1, 1, W, n_kv, d), torch.bfloat16, g)
+            inputs[l] = (W, synth.to_raw(q), synth.to_raw(k), synth.to_raw(v))
+        return inputs[l]
+
+    def call(l):
+        W, qr, kr, vr = layer_inputs(l)
+        t = time.time()
+        oracle.decode(windows[l:l + 1], [L], qr, kr, vr, [L - W], 1.0 / math.sqrt(d))
+        return time.time() - t
+
+    spent = step_s = 0.0
+    calls = 0
     per_layer_s = target_s / n_layers
     for l in range(n_layers):
-        W = int(windows[l].max())
-        g = synth.gen(9000 + l)
-        q = synth.randn((1, 1, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
-        k = synth.randn((1, 1, W, n_kv, d), torch.bfloat16, g)
-        v = synth.randn((1, 1, W, n_kv, d), torch.bfloat16, g)
-        qr, kr, vr = synth.to_raw(q), synth.to_raw(k), synth.to_raw(v)
         layer_s, reps = 0.0, 0
         while reps == 0 or layer_s < per_layer_s:
-            t = time.time()
-            oracle.decode(windows[l:l + 1], [L], qr, kr, vr, [L - W], 1.0 / math.sqrt(d))
-            layer_s += time.time() - t
+            layer_s += call(l)
             reps += 1
         spent += layer_s
         step_s += layer_s / reps
         calls += reps
-    return {"value": round(1.0 / step_s, 4), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "the full 48-layer decode step (%.2f GB of K/V), %d oracle calls of one "
-                      "layer each, %.1f s in total; step time = sum over layers of the mean "
-                      "call time" % (total_bytes / 1e9, calls, spent),
-            "kv_read_gbps": round(total_bytes / step_s / 1e9, 3),
-            "gpu_over_cpu": round(gpu_tok_s * step_s, 1)}
+        inputs.pop(l, None)
+    res = {"value": round(1.0 / step_s, 4), "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": "the full 48-layer decode step (%.2f GB of K/V), %d oracle calls of one "
+                     "layer each on %d threads, %.1f s in total; step time = sum over layers "
+                     "of the mean call time" % (total_bytes / 1e9, calls, threads, spent),
+           "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+           "kv_read_gbps": round(total_bytes / step_s / 1e9, 3),
+           "gpu_over_cpu": round(gpu_tok_s * step_s, 1)}
+
+    # one thread: layers in order until about half the budget is spent
+    oracle.set_threads(1)
+    try:
+        t1, b1, used = 0.0, 0.0, 0
+        for l in range(n_layers):
+            t1 += call(l)
+            b1 += float(layer_bytes[l])
+            used += 1
+            inputs.pop(l, None)
+            if t1 >= target_s / 2:
+                break
+    finally:
+        oracle.set_threads(threads)
+    step_1t = t1 * total_bytes / b1
+    res["one_thread"] = {"tokens_per_s": round(1.0 / step_1t, 5),
+                         "step_s_extrapolated": round(step_1t, 2),
+                         "sample": "layers 0-%d of the step (%.2f of %.2f GB) on 1 thread in "
+                                   "%.1f s, extrapolated by K/V bytes" %
+                                   (used - 1, b1 / 1e9, total_bytes / 1e9, t1)}
+
+    # the 161K chunked prefill on sampled rows
+    n_seqs, n, P = 4, 2048, synth.CTX_161K
+    wl = np.array(synth.YAML_LAYER0, np.int32)
+    cap = int(((wl.astype(np.int64) + 15) // 16 * 16).max())
+    g = synth.gen(9100)
+    dev = torch.device("cuda", 0) if torch.cuda.is_available() else torch.device("cpu")
+    gd = synth.gen(9100, dev)
+    kh = synth.to_raw(synth.randn((n_seqs, cap, n_kv, d), torch.bfloat16, gd))
+    vh = synth.to_raw(synth.randn((n_seqs, cap, n_kv, d), torch.bfloat16, gd))
+    qc = synth.to_raw(synth.randn((n_seqs, n, n_kv * G, d), torch.bfloat16, g,
+                                  std=1.0 / math.sqrt(d)))
+    kc = synth.to_raw(synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g))
+    vc = synth.to_raw(synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g))
+    rows = np.linspace(0, n - 1, 16).astype(np.int64)
+    t = time.time()
+    oracle.prefill(wl, [P] * n_seqs, qc, kc, vc, kh, vh, [P - cap] * n_seqs,
+                   1.0 / math.sqrt(d), rows=rows)
+    t_rows = time.time() - t
+    chunk_s = t_rows * n / rows.size
+    pf = {"chunk_step_s_extrapolated": round(chunk_s, 2),
+          "tokens_per_s": round(n_seqs * n / chunk_s, 2),
+          "sample": "16 evenly spaced rows of the 2048-row chunk, all 4 sequences and 24 "
+                    "query heads, on %d threads in %.1f s, extrapolated by the row count"
+                    % (threads, t_rows)}
+    if gpu_prefill:
+        pf["gpu_over_cpu"] = round(chunk_s / (gpu_prefill["prefill_ms"] / 1e3), 1)
+    res["prefill_161k"] = pf
+    del kh, vh, qc, kc, vc
+
+    # the continuous batch: same 48-layer stack, 32 contexts in [4K, 160K]
+    Lcb = synth.cb_contexts()
+    w64 = windows.astype(np.int64).reshape(-1)
+    cb_bytes = float(np.minimum(w64[None, :], Lcb[:, None]).sum()) * KV_BYTES_PER_TOK_HEAD
+    cb_step_s = step_s * cb_bytes / total_bytes
+    res["continuous_batch"] = {"tokens_per_s": round(len(Lcb) / cb_step_s, 4),
+                               "sample": "extrapolated from the all-thread 48-layer step by K/V "
+                                         "bytes per step (%.1f GB)" % (cb_bytes / 1e9)}
+    return res
 
 
 if __name__ == "__main__":

@@ -324,21 +324,12 @@ __device__ __forceinline__ void process_block(BlockRegs<T, D, G>& br, const bool
 // of the stream's bandwidth, streamed stores about a third of that.  A small
 // launch (one layer at batch 1) is latency-bound instead, and ordinary
 // stores let the merge stage read the records back ~4% sooner per step.
-// Records that another workgroup of the same launch reads (fused step) are
-// stored and loaded as relaxed agent-scope atomics, i.e. accesses that are
-// coherent across the XCDs' separate L2 caches by themselves, so no
-// whole-cache write-back or invalidate is needed to hand them over.
-__device__ __forceinline__ void rec_put(float* p, float v, bool coherent, bool streamed) {
-    if (coherent)
-        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else if (streamed)
+__device__ __forceinline__ void rec_put(float* p, float v, bool streamed) {
+    if (streamed)
         __builtin_nontemporal_store(v, p);
     else  // an ordinary store, written as a relaxed atomic so that the
           // compiler cannot fold it into the non-temporal one above
         __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ float rec_get(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Output row of (layer, sequence, kv head): G query heads x D, fp32, bf16 or fp16.
@@ -375,14 +366,6 @@ struct MergeCfg {
     static_assert(NE4 % DS == 0, "merge geometry");
 };
 
-template <bool COH>
-__device__ __forceinline__ float rec_load(const float* p) {
-    if constexpr (COH)
-        return rec_get(p);
-    else
-        return *p;
-}
-
 // factor that takes a partial kept at running maximum `from` to maximum `to`
 __device__ __forceinline__ float rescale(float from, float to) {
     return from == to ? 1.f : fast_exp2(from - to);
@@ -390,7 +373,7 @@ __device__ __forceinline__ float rescale(float from, float to) {
 
 // One pass over the splits s = k, k + SG, ... of column c (query head h):
 // running maximum m and num = sum 2^(m_s - m) acc_s[c].
-template <int D, int G, bool COH>
+template <int D, int G>
 __device__ __forceinline__ f32x4 merge_num_part(const float* rec0, int rec_floats, int ns, int k,
                                                 int c) {
     typedef MergeCfg<D, G> M;
@@ -400,13 +383,8 @@ __device__ __forceinline__ f32x4 merge_num_part(const float* rec0, int rec_float
 #pragma unroll 8
     for (int s = k; s < ns; s += M::SG) {
         const float* rs = rec0 + (int64_t)s * rec_floats;
-        const float ms = rec_load<COH>(rs + G * D + h);
-        f32x4 v;
-        if constexpr (COH)
-            v = f32x4{rec_get(rs + c * 4), rec_get(rs + c * 4 + 1), rec_get(rs + c * 4 + 2),
-                      rec_get(rs + c * 4 + 3)};
-        else
-            v = *reinterpret_cast<const f32x4*>(rs + c * 4);
+        const float ms = rs[G * D + h];
+        const f32x4 v = *reinterpret_cast<const f32x4*>(rs + c * 4);
         const float mn = fmaxf(m, ms);
         const float al = rescale(m, mn), f = fast_exp2(ms - mn);
         num.x = fmaf(f, v.x, num.x * al);
@@ -420,7 +398,7 @@ __device__ __forceinline__ f32x4 merge_num_part(const float* rec0, int rec_float
 
 // The same pass for the denominator of head h: running maximum (returned in
 // m) and sum 2^(m_s - m) l_s.
-template <int D, int G, bool COH>
+template <int D, int G>
 __device__ __forceinline__ float merge_den_part(const float* rec0, int rec_floats, int ns, int k,
                                                 int h, float& m) {
     typedef MergeCfg<D, G> M;
@@ -429,8 +407,8 @@ __device__ __forceinline__ float merge_den_part(const float* rec0, int rec_float
 #pragma unroll 8
     for (int s = k; s < ns; s += M::SG) {
         const float* rs = rec0 + (int64_t)s * rec_floats;
-        const float ms = rec_load<COH>(rs + G * D + h);
-        const float ls = rec_load<COH>(rs + G * D + G + h);
+        const float ms = rs[G * D + h];
+        const float ls = rs[G * D + G + h];
         const float mn = fmaxf(m, ms);
         den = fmaf(fast_exp2(ms - mn), ls, den * rescale(m, mn));
         m = mn;
@@ -441,7 +419,7 @@ __device__ __forceinline__ float merge_den_part(const float* rec0, int rec_float
 // Merge of column chunks [ds0, ds1) of one (layer, sequence, kv head) by the
 // NTHREADS threads of a workgroup.  obase: output offset of the head's first
 // element.
-template <int D, int G, bool COH, int NTHREADS>
+template <int D, int G, int NTHREADS>
 __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0, int ds1, void* out,
                              int out_kind, int64_t obase) {
     typedef MergeCfg<D, G> M;
@@ -454,12 +432,12 @@ __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0,
     for (int pr = t; pr < npairs; pr += NTHREADS) {
         if (pr < ncols * M::SG) {
             const int cl = pr % ncols, k = pr / ncols;
-            s_num[k][cl] = merge_num_part<D, G, COH>(rec0, rec_floats, ns, k, c0 + cl);
+            s_num[k][cl] = merge_num_part<D, G>(rec0, rec_floats, ns, k, c0 + cl);
         } else {
             const int q = pr - ncols * M::SG;
             const int h = q / M::SG, k = q % M::SG;
             float m;
-            s_den[k][h] = merge_den_part<D, G, COH>(rec0, rec_floats, ns, k, h, m);
+            s_den[k][h] = merge_den_part<D, G>(rec0, rec_floats, ns, k, h, m);
             s_mk[k][h] = m;
         }
     }
@@ -486,13 +464,13 @@ __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0,
 }
 
 // The merge of one (layer, sequence, kv head) done by the 256 threads of the
-// split workgroup that finished last (records read with agent-coherent
-// loads): the same operations in the same order as decode_merge_kernel.
+// split workgroup that finished last: the same operations in the same order
+// as decode_merge_kernel.
 template <int D, int G>
 __device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, void* out, int out_kind,
                                    int64_t obase) {
-    merge_chunks<D, G, true, kThreads>(rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, out_kind,
-                                       obase);
+    merge_chunks<D, G, kThreads>(rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, out_kind,
+                                 obase);
 }
 
 // Split-kernel modes: plain split stage; split stage that also appends the
@@ -563,19 +541,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 
     // Fused step: after this workgroup's record is written, count its arrival;
     // the last of the head's ns splits merges all of them and re-arms the
-    // counter (nothing waits, so no workgroup can hang on another).  The
-    // record stores are agent-coherent; waiting for all of them to complete
-    // (vmcnt 0) before the workgroup barrier and the counter increment makes
-    // them visible to whichever workgroup draws the last ticket, which reads
-    // them with agent-coherent loads.
+    // counter (nothing waits, so no workgroup can hang on another).  Memory
+    // ordering, agent scope (the workgroups run on different XCDs, each with
+    // its own L2): the barrier orders every thread's record stores before
+    // thread 0's counter increment, which is a release; the workgroup whose
+    // increment returns ns - 1 has read the end of that release sequence, so
+    // its acquire fence makes every split's record visible, and the barrier
+    // after it hands that on to the other threads before they read.
     auto arrive_and_merge = [&]() {
         if constexpr (FUSED) {
             __shared__ uint32_t s_old;
             uint32_t* cnt = a.counters + ((int64_t)rel_layer * a.n_kv_heads + hd.head) * a.n_seqs + b;
-            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (threadIdx.x == 0)
-                s_old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (threadIdx.x == 0) {
+                const uint32_t old =
+                    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                if (old == (uint32_t)(ns - 1)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                s_old = old;
+            }
             __syncthreads();
             if (s_old != (uint32_t)(ns - 1)) return;
             const float* rec0 =
@@ -587,10 +570,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 
     const int64_t slot = a.seq_slots ? (int64_t)a.seq_slots[b] : (int64_t)b;
     if (slot < 0 || slot >= a.table_rows) {  // invalid slot: an empty record -> NaN output
-        for (int e = threadIdx.x; e < G * D; e += kThreads) rec_put(rec + e, 0.f, FUSED, streamed);
+        for (int e = threadIdx.x; e < G * D; e += kThreads) rec_put(rec + e, 0.f, streamed);
         if (threadIdx.x < G) {
-            rec_put(rec + G * D + threadIdx.x, -INFINITY, FUSED, streamed);
-            rec_put(rec + G * D + G + threadIdx.x, 0.f, FUSED, streamed);
+            rec_put(rec + G * D + threadIdx.x, -INFINITY, streamed);
+            rec_put(rec + G * D + G + threadIdx.x, 0.f, streamed);
         }
         arrive_and_merge();
         return;
@@ -756,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         float sum = 0.f;
 #pragma unroll
         for (int sl = 0; sl < 2 * kWaves; sl++) sum += s_acc[sl][e];
-        rec_put(rec + e, sum, FUSED, streamed);
+        rec_put(rec + e, sum, streamed);
     }
     if (threadIdx.x < G) {
         const int h = threadIdx.x;
@@ -766,8 +749,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
 #pragma unroll
         for (int sl = 0; sl < 2 * kWaves; sl++) lsum += s_l[sl][h];
-        rec_put(rec + G * D + h, MW, FUSED, streamed);
-        rec_put(rec + G * D + G + h, lsum, FUSED, streamed);
+        rec_put(rec + G * D + h, MW, streamed);
+        rec_put(rec + G * D + G + h, lsum, streamed);
     }
     arrive_and_merge();
 }
@@ -801,8 +784,8 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     const int ns = (int)((n + a.split_tokens - 1) / a.split_tokens);
     const float* rec0 =
         a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
-    merge_chunks<D, G, false, M::THREADS>(rec0, ns, a.rec_floats, ds0, ds0 + a.merge_chunks, a.out,
-                                          a.out_kind, obase);
+    merge_chunks<D, G, M::THREADS>(rec0, ns, a.rec_floats, ds0, ds0 + a.merge_chunks, a.out,
+                                   a.out_kind, obase);
 }
 
 template <int T, int D, int G, int MODE>
