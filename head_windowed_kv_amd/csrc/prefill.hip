@@ -170,11 +170,23 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
+// Kernel passes.  kFast: P (and, for bf16 caches, V) in fp16, one P.V
+// product.  kExact (bf16 caches): P split into a truncated bf16 part and a
+// bf16 remainder, two products.  kRedo (bf16 caches): the second launch of
+// hwkv_prefill_attn.  kFast writes a row whose result is non-finite or whose
+// largest magnitude is below 2^-12 of its softmax sum (where the V
+// conversion's absolute error could matter) as NaN; kRedo reads the first
+// element of each row of its workgroup, exits at once if none is NaN, and
+// otherwise runs the kExact pass and rewrites exactly those rows (a row that
+// is NaN by rule, e.g. a bad slot, comes out NaN again).  Keeping the exact
+// pass out of the fast kernel leaves it fewer registers to hold.
+constexpr int kFast = 0, kExact = 1, kRedo = 2;
+
 // BIG: cache blocks of more than 16 tokens (the 16-token case keeps every
-// slice address a compile-time constant).  EXACT (bf16 caches): only the pass
-// with P split into two bf16 products.
-template <int KT, int D, int G, bool BIG, bool EXACT>
+// slice address a compile-time constant).
+template <int KT, int D, int G, bool BIG, int PASS>
 __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(PrefillArgs a) {
+    static_assert(KT == kBF16 || PASS == kFast, "fp16 caches have a single pass");
     typedef PfCfg<D> C;
     // two stages of K and V tiles; separate objects so that the compiler sees
     // that a DMA into one stage never aliases the reads of the other
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TILE];
-    __shared__ int s_redo;  // a workgroup's fp16 pass must be redone exactly
+    __shared__ int s_redo;  // kRedo: some row of the workgroup needs the exact pass
     // per wave: the last history key position it staged from a block whose
     // id lies outside the pool; the rows whose window reaches it are NaN
     __shared__ int64_t s_bad_hi[kWaves];
@@ -225,7 +237,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         return;
     }
     if (pair >= a.n_kv_heads * a.n_seqs) return;
-    if (threadIdx.x == 0) s_redo = 0;  // read only after later barriers
     const int rank = pair / a.n_seqs;
     const int b = pair % a.n_seqs;
     const int kvh = a.order[(int64_t)a.layer * a.n_kv_heads + rank];
@@ -251,6 +262,28 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     const int64_t T0 = kmin / kBK;
     const int n_tiles = (int)(pmax / kBK - T0 + 1);
     const int64_t wq_last = p0 + kQW - 1 < P + n - 1 ? p0 + kQW - 1 : P + n - 1;
+
+    // kRedo: the rows kFast marked (NaN in their first element)
+    bool redo_row = false;
+    if constexpr (PASS == kRedo) {
+        if (threadIdx.x == 0) s_redo = 0;
+        __syncthreads();
+        const int64_t r = p0 - P + col;
+        if (wave_on && r < n) {
+            const int64_t at = (((int64_t)b * n + r) * a.n_q_heads + (int64_t)kvh * G + qg) * D;
+            float o0;
+            if (a.out_kind == kBF16)
+                o0 = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.out)[at] << 16);
+            else if (a.out_kind == kF16)
+                o0 = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(a.out)[at]);
+            else
+                o0 = reinterpret_cast<const float*>(a.out)[at];
+            redo_row = __builtin_isnan(o0);
+        }
+        if (__builtin_amdgcn_ballot_w64(redo_row) != 0 && lane == 0) s_redo = 1;
+        __syncthreads();
+        if (!s_redo) return;  // uniform over the workgroup
+    }
 
     const int32_t* tbl = a.block_ids + (seq_ok ? slot : 0) * a.blocks_per_seq + hd.table_off;
     const const_i32* tblc = (const const_i32*)tbl;
@@ -599,39 +632,27 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         }
     };
 
-    if constexpr (KT == kBF16 && EXACT) {
-        run(BoolC<false>{});
-    } else if constexpr (KT == kBF16) {
-        // First pass with P and V in fp16 (one PV product).  The conversion
-        // of V is exact for |v| in [2^-14, 65504]; a larger value becomes inf
-        // and poisons its output column (inf or NaN), and smaller values lose
-        // at most 2^-25 each.  A workgroup in which some live row came out
-        // non-finite, or with a maximum below 2^-12 (where that absolute error
-        // could matter), runs again with P split into two bf16 products and
-        // the bf16 V tiles as stored.
-        run(BoolC<true>{});
-        if (wave_on) {
-            float sa = 0.f, mx = 0.f;
+    if constexpr (PASS == kFast)
+        run(BoolC<true>{});  // P in fp16 (bf16 caches: V converted to fp16 in LDS)
+    else
+        run(BoolC<false>{});  // P as a truncated bf16 part and a bf16 remainder
+
+    // kFast on bf16 caches: does this lane's row need the exact pass?
+    bool mark = false;
+    if constexpr (PASS == kFast && KT == kBF16) {
+        float sa = 0.f, mx = 0.f;
 #pragma unroll
-            for (int db = 0; db < C::DBLK; db++)
+        for (int db = 0; db < C::DBLK; db++)
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const float x = fabsf(oacc[db][i]);
-                    sa += x;
-                    mx = fmaxf(mx, x);
-                }
-            const f32x2 mp = with_partner(mx), lp = with_partner(l_run);
-            mx = fmaxf(mp.x, mp.y);
-            const float l_tot = lp.x + lp.y;
-            const bool ok = __builtin_isfinite(sa) && __builtin_isfinite(l_tot) &&
-                            mx >= 0x1p-12f * l_tot;
-            const bool live = p0 - P + col < n && seq_ok;
-            if (__builtin_amdgcn_ballot_w64(live && !ok) != 0 && lane == 0) s_redo = 1;
-        }
-        __syncthreads();
-        if (s_redo) run(BoolC<false>{});
-    } else {
-        run(BoolC<true>{});
+            for (int i = 0; i < 16; i++) {
+                const float x = fabsf(oacc[db][i]);
+                sa += x;
+                mx = fmaxf(mx, x);
+            }
+        const f32x2 mp = with_partner(mx), sp = with_partner(sa), lp2 = with_partner(l_run);
+        const float l_tot2 = lp2.x + lp2.y;
+        mark = !(__builtin_isfinite(sp.x + sp.y) && __builtin_isfinite(l_tot2) &&
+                 fmaxf(mp.x, mp.y) >= 0x1p-12f * l_tot2);
     }
 
     // ---- normalise and write this lane's query row ----
@@ -646,8 +667,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     if (!wave_on || r >= n) return;
     // NaN for a bad sequence, and for a row whose window [p - w + 1, p]
     // reaches a history key held by a block outside the pool
-    const bool row_ok = seq_ok && lost < p0 + col - w + 1;
+    const bool row_ok = seq_ok && lost < p0 + col - w + 1 && !mark;
     const float inv = row_ok ? 1.0f / l_tot : __builtin_nanf("");
+    if (PASS == kRedo && !redo_row) return;  // kFast's row stands
     const int64_t obase = (((int64_t)b * n + r) * a.n_q_heads + (int64_t)kvh * G + qg) * D;
 #pragma unroll
     for (int db = 0; db < C::DBLK; db++)
@@ -668,15 +690,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         }
 }
 
-template <int T, int D, int G>
-hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
-    auto kernel = a.tpb_log2 > 0 ? prefill_kernel<T, D, G, true, false>
-                                 : prefill_kernel<T, D, G, false, false>;
-    if constexpr (T == kBF16) {
-        if (a.exact_p)
-            kernel = a.tpb_log2 > 0 ? prefill_kernel<T, D, G, true, true>
-                                    : prefill_kernel<T, D, G, false, true>;
-    }
+template <int T, int D, int G, bool BIG>
+hwkv_status launch_pass(const PrefillArgs& a, int pass, hipStream_t s) {
+    auto kernel = prefill_kernel<T, D, G, BIG, kFast>;
+    if constexpr (T == kBF16)
+        kernel = pass == kExact ? prefill_kernel<T, D, G, BIG, kExact>
+                 : pass == kRedo ? prefill_kernel<T, D, G, BIG, kRedo>
+                                 : prefill_kernel<T, D, G, BIG, kFast>;
     const int n_pb = (a.n_chunk + kQW - 1) / kQW;
     const int n_units = G * n_pb;
     const int64_t n_groups = (n_units + kWaves - 1) / kWaves;
@@ -689,6 +709,18 @@ hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
     if (e != hipSuccess)
         return fail(HWKV_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
     return HWKV_OK;
+}
+
+// bf16 caches: the exact entry runs kExact; the default entry runs kFast and
+// then kRedo (which exits at once unless a workgroup needs the exact pass).
+// fp16 caches: one kFast launch.
+template <int T, int D, int G>
+hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
+    auto run = a.tpb_log2 > 0 ? launch_pass<T, D, G, true> : launch_pass<T, D, G, false>;
+    if (T == kBF16 && a.exact_p) return run(a, kExact, s);
+    const hwkv_status st = run(a, kFast, s);
+    if (st != HWKV_OK || T != kBF16) return st;
+    return run(a, kRedo, s);
 }
 
 #define HWKV_FOR_GROUPS(X) X(1) X(2) X(3) X(4) X(6) X(8)

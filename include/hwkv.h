@@ -393,11 +393,15 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * once to fp16 (11 significant bits; row error a few 1e-4 of the row's
  * largest output on N(0,1) data).  For BF16 caches this needs V in fp16:
  * each V tile is converted in on-chip memory, which is exact for |v| in
- * [2^-14, 65504].  A workgroup with a non-finite output (a V element
- * beyond fp16's range) or with a row whose largest output magnitude is below
- * 2^-12 (where the conversion's absolute error, at most 2^-25 per element,
- * could matter) is recomputed as hwkv_prefill_attn_exact does, so such
- * inputs cost time, not accuracy. */
+ * [2^-14, 65504].  A query row whose result comes out non-finite (a V
+ * element beyond fp16's range) or whose largest magnitude is below 2^-12 of
+ * its softmax sum (where the conversion's absolute error, at most 2^-25 per
+ * element, could matter) is recomputed as hwkv_prefill_attn_exact does, so
+ * such inputs cost time, not accuracy.  For BF16 caches the call enqueues two
+ * kernels: the fp16 pass, which writes such rows as NaN, and a second pass
+ * that exits at once unless a row of its workgroup is NaN, in which case it
+ * recomputes the workgroup exactly and rewrites those rows (rows that are NaN
+ * by the rules above come out NaN again). */
 hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer, int32_t n_seqs,
                               const int32_t *seq_slots, const int64_t *pos0,

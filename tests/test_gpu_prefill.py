@@ -321,9 +321,10 @@ def test_exact_variant_and_fp16_p_error(d, G):
 def test_v_beyond_fp16_range_falls_back_to_exact(d):
     """V elements of +-2^20 (finite in bf16, beyond fp16's 65504) in the
     history and in the chunk: the fp16 pass of every workgroup that reads them
-    turns non-finite, so those workgroups redo their rows exactly; all rows
+    turns non-finite, so those rows are redone exactly; all rows
     match the oracle, and the rows that attend to the large values equal the
-    exact variant bit for bit."""
+    exact variant bit for bit (the fast pass marks every row whose result is
+    non-finite, and the second pass recomputes exactly those)."""
     big = 2.0 ** 20
     P, n = 3000, 130
     hist_pos, chunk_row = P - 5, 10
@@ -352,8 +353,8 @@ def test_v_beyond_fp16_range_falls_back_to_exact(d):
 @pytest.mark.parametrize("d", [128, 64, 256])
 def test_tiny_v_falls_back_to_exact(d):
     """V of kv head 1 scaled by 2^-20 (|v| ~ 1e-6: normal in bf16, subnormal
-    in fp16): its outputs are far below 2^-12, so its workgroups redo their
-    rows exactly (bit for bit the exact variant) while the other heads keep
+    in fp16): its outputs are far below 2^-12 of their softmax sums, so its
+    rows are redone exactly (bit for bit the exact variant) while the other heads keep
     the fp16 pass; every row matches the oracle."""
     def edit(v, b, p0):
         v[..., 1, :] *= 2.0 ** -20
