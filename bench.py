@@ -177,7 +177,7 @@ def summarize_counters(fetch_dir, write_dir, split_tokens):
     out = {"kernel_source_sha": kernel_source_sha(), "probe_copy_bytes": PROBE_COPY_BYTES,
            "split_tokens": lay.desc().split_tokens,
            "command": "rocprofv3 --pmc <COUNTER> --output-format csv -d <dir> -o run -- "
-                      "python -u bench.py --counter-pass --steps 3 --warmup 1"}
+                      "python -u bench.py --counter-pass --steps 3 --warmup 2"}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(folder, counter)
         split = [v for n, v in rows if "decode_split_kernel" in n]
