@@ -566,6 +566,12 @@ def prefill_leg(H, torch, synth):
     pos = torch.full((n_seqs,), P, dtype=torch.int64, device=dev)
     scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream()
+    # the default entry's workspace: the fp16 copy of the V rows it reads
+    pws = H.make_prefill_workspace(lay, 0, n_seqs, n, device=dev)
+    pws_bytes = int(pws.numel())
+
+    def fast(*a):
+        H.hwkv_prefill_attn(*a[:6], pws, *a[6:])
 
     def median_ms(fn, reps=10):
         for _ in range(2):
@@ -582,7 +588,7 @@ def prefill_leg(H, torch, synth):
         return sorted(ts)[len(ts) // 2]
     # P in fp16 (the default entry) and P split into two bf16 products
     exact_ms = median_ms(H.hwkv_prefill_attn_exact, 5)
-    pf_ms = median_ms(H.hwkv_prefill_attn)
+    pf_ms = median_ms(fast)
     # algorithmic flops: per query row and query head, 4 d flops per key in
     # its window [p-w+1, p] (QK^T and PV, 2 flops per multiply-add)
     keys = 0
@@ -622,7 +628,7 @@ def prefill_leg(H, torch, synth):
     dec_ms = e0.elapsed_time(e1) / n_dec
     dec_bytes = float(np.minimum(w.astype(np.int64), P + n + n_warm).sum()) * n_seqs * \
         KV_BYTES_PER_TOK_HEAD
-    del cache
+    del cache, pws
     torch.cuda.empty_cache()
     gemm_tf = gemm_reference_tflops(torch)
     return {"workload": "4 seqs x 1 layer, 2048-token chunk at P=164864, windows 4096x2/16384x2/"
@@ -633,7 +639,9 @@ def prefill_leg(H, torch, synth):
             "gemm_reference_tflops": round(gemm_tf, 1),
             "frac_of_gemm_reference": round(flop / (pf_ms / 1e3) / 1e12 / gemm_tf, 4),
             "prefill_tokens_per_s": round(n_seqs * n / (pf_ms / 1e3), 1),
-            "p_in_pv_product": "fp16 (V converted to fp16 on chip; exact re-run if out of range)",
+            "p_in_pv_product": "fp16 (V copied to fp16 by a pre-pass; exact re-run of rows out "
+                               "of range)",
+            "prefill_workspace_bytes": pws_bytes,
             "prefill_exact_ms": round(exact_ms, 4),
             "prefill_exact_tflops": round(flop / (exact_ms / 1e3) / 1e12, 1),
             "chunk_append_ms": round(append_ms, 4),

@@ -29,7 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 HWKV_F32 = 0
 HWKV_BF16 = 1
 HWKV_F16 = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {0: "HWKV_OK", 1: "HWKV_ERR_INVALID_ARG", 2: "HWKV_ERR_UNSUPPORTED",
                 3: "HWKV_ERR_MISALIGNED", 4: "HWKV_ERR_CAPACITY", 5: "HWKV_ERR_ABI_MISMATCH",
@@ -43,7 +43,7 @@ EXPORTED = ("hwkv_abi_version", "hwkv_last_error", "hwkv_layout_create", "hwkv_l
             "hwkv_decode_attn", "hwkv_decode_split_append", "hwkv_decode_append_attn",
             "hwkv_decode_append_attn_static", "hwkv_step_workspace_bytes",
             "hwkv_decode_step",
-            "hwkv_prefill_attn", "hwkv_prefill_attn_exact")
+            "hwkv_prefill_workspace_bytes", "hwkv_prefill_attn", "hwkv_prefill_attn_exact")
 
 
 class hwkv_layout_desc(ctypes.Structure):
@@ -117,10 +117,14 @@ _lib.hwkv_step_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _i32, _P(_u64)
 _lib.hwkv_decode_step.restype = ctypes.c_int
 _lib.hwkv_decode_step.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                   _i32, _vp, _f32, _vp, _u64, _vp, ctypes.c_int, _vp]
-for _name in ("hwkv_prefill_attn", "hwkv_prefill_attn_exact"):
-    getattr(_lib, _name).restype = ctypes.c_int
-    getattr(_lib, _name).argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _vp, _vp, _i32, _i32, _vp,
-                                     _vp, _vp, _vp, ctypes.c_int, _f32, _vp]
+_lib.hwkv_prefill_workspace_bytes.restype = ctypes.c_int
+_lib.hwkv_prefill_workspace_bytes.argtypes = [_vp, _i32, _i32, _i32, _P(_u64)]
+_lib.hwkv_prefill_attn.restype = ctypes.c_int
+_lib.hwkv_prefill_attn.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _vp, _vp, _i32, _i32, _vp,
+                                   _vp, _vp, _vp, _u64, _vp, ctypes.c_int, _f32, _vp]
+_lib.hwkv_prefill_attn_exact.restype = ctypes.c_int
+_lib.hwkv_prefill_attn_exact.argtypes = [_vp, _P(hwkv_cache), _i32, _i32, _vp, _vp, _i32, _i32,
+                                         _vp, _vp, _vp, _vp, ctypes.c_int, _f32, _vp]
 
 
 class HwkvError(RuntimeError):
@@ -517,23 +521,39 @@ def hwkv_decode_step(cache: Cache, layer_begin: int, n_layers: int, pos: torch.T
                         q, scale, workspace, out, seq_slots, stream)
 
 
+def hwkv_prefill_workspace_bytes(layout: Layout, layer: int, n_seqs: int, n_chunk: int) -> int:
+    b = ctypes.c_uint64()
+    _check(_lib.hwkv_prefill_workspace_bytes(layout.handle, layer, n_seqs, n_chunk,
+                                             ctypes.byref(b)))
+    return int(b.value)
+
+
+def make_prefill_workspace(layout: Layout, layer: int, n_seqs: int, n_chunk: int,
+                           device="cuda") -> torch.Tensor:
+    """Workspace of hwkv_prefill_attn (at least 256 bytes, so never empty)."""
+    return _alloc_aligned(max(hwkv_prefill_workspace_bytes(layout, layer, n_seqs, n_chunk), 256),
+                          device)
+
+
 def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,
-                      k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, scale: float,
-                      seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
+                      k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+                      out: torch.Tensor, scale: float, seq_slots: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
     """q, out: [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: [n_seqs][n_chunk][n_kv][head_dim].
-    P enters the P.V product in fp16."""
-    _prefill(_lib.hwkv_prefill_attn, cache, layer, pos0, q, k, v, out, scale, seq_slots, stream)
+    P enters the P.V product in fp16; workspace: make_prefill_workspace."""
+    _prefill(_lib.hwkv_prefill_attn, cache, layer, pos0, q, k, v, workspace, out, scale,
+             seq_slots, stream)
 
 
 def hwkv_prefill_attn_exact(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,
                             k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, scale: float,
                             seq_slots: Optional[torch.Tensor] = None, stream=None) -> None:
-    """hwkv_prefill_attn with P split into two bf16 products for bf16 caches."""
-    _prefill(_lib.hwkv_prefill_attn_exact, cache, layer, pos0, q, k, v, out, scale, seq_slots,
-             stream)
+    """hwkv_prefill_attn with P split into two bf16 products for bf16 caches (no workspace)."""
+    _prefill(_lib.hwkv_prefill_attn_exact, cache, layer, pos0, q, k, v, None, out, scale,
+             seq_slots, stream)
 
 
-def _prefill(fn, cache, layer, pos0, q, k, v, out, scale, seq_slots, stream) -> None:
+def _prefill(fn, cache, layer, pos0, q, k, v, workspace, out, scale, seq_slots, stream) -> None:
     d = cache.layout.desc()
     n_seqs, n_chunk, n_q = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     _expect("q", q, (n_seqs, n_chunk, n_q, d.head_dim), torch_dtype(d.dtype))
@@ -545,9 +565,16 @@ def _prefill(fn, cache, layer, pos0, q, k, v, out, scale, seq_slots, stream) -> 
     _expect("pos0", pos0, (n_seqs,), torch.int64)
     _expect_opt("seq_slots", seq_slots, (n_seqs,), torch.int32)
     cv = cache.view()
-    _check(fn(cache.layout.handle, ctypes.byref(cv), layer, int(q.shape[0]), _ptr(seq_slots),
-              _ptr(pos0), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-              _dtype_code(out.dtype), scale, _stream(stream)))
+    head = (cache.layout.handle, ctypes.byref(cv), layer, int(q.shape[0]), _ptr(seq_slots),
+            _ptr(pos0), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(k), _ptr(v))
+    tail = (_ptr(out), _dtype_code(out.dtype), scale, _stream(stream))
+    if fn is _lib.hwkv_prefill_attn:
+        if workspace is None or workspace.dtype != torch.uint8 or workspace.device != out.device:
+            raise ValueError("workspace must be a uint8 tensor on the device of out "
+                             "(make_prefill_workspace)")
+        _check(fn(*head, _ptr(workspace), workspace.numel(), *tail))
+    else:
+        _check(fn(*head, *tail))
 
 
 def loaded_library_path() -> str:

@@ -396,11 +396,38 @@ hwkv_status hwkv_decode_step(const hwkv_layout* L, const hwkv_cache* c, int32_t 
     return launch_decode_step(*L, group, a, stream);
 }
 
+hwkv_status hwkv_prefill_workspace_bytes(const hwkv_layout* L, int32_t layer, int32_t n_seqs,
+                                         int32_t n_chunk, uint64_t* bytes) {
+    clear_error();
+    if (!L || !bytes) return fail(HWKV_ERR_INVALID_ARG, "null layout or bytes");
+    if (layer < 0 || layer >= L->n_layers)
+        return fail(HWKV_ERR_INVALID_ARG, "layer " + std::to_string(layer) + " outside the layout's " +
+                                              std::to_string(L->n_layers) + " layers");
+    if (n_seqs < 1 || n_chunk < 1) return fail(HWKV_ERR_INVALID_ARG, "n_seqs and n_chunk must be >= 1");
+    *bytes = 0;
+    if (L->dtype != HWKV_BF16) return HWKV_OK;  // only bf16 caches take the fp16 copy
+    const uint64_t row = (uint64_t)L->head_dim * 2;
+    for (int32_t h = 0; h < L->n_kv_heads; h++) {
+        const uint64_t rows = (uint64_t)L->windows[(size_t)layer * L->n_kv_heads + h] - 1 + n_chunk;
+        if (rows * row >= (1ull << 31))
+            return fail(HWKV_ERR_UNSUPPORTED,
+                        "kv head " + std::to_string(h) + ": window - 1 + n_chunk = " +
+                            std::to_string(rows) + " fp16 V rows take 2^31 bytes or more "
+                            "(hwkv_prefill_attn_exact needs no workspace)");
+    }
+    const uint64_t per_seq = (uint64_t)prefill_v16_rows(*L, layer, n_chunk) * row;
+    if (per_seq > UINT64_MAX / (uint64_t)n_seqs)
+        return fail(HWKV_ERR_OVERFLOW, "prefill workspace size overflows 64 bits");
+    *bytes = per_seq * (uint64_t)n_seqs;
+    return HWKV_OK;
+}
+
 static hwkv_status prefill_entry(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
                                  int32_t n_seqs, const int32_t* seq_slots, const int64_t* pos0,
                                  int32_t n_chunk, int32_t n_q_heads, const void* q,
-                                 const void* k, const void* v, void* out, hwkv_dtype out_dtype,
-                                 float scale, bool exact_p, hipStream_t stream) {
+                                 const void* k, const void* v, void* ws, uint64_t ws_bytes,
+                                 void* out, hwkv_dtype out_dtype, float scale, bool exact_p,
+                                 hipStream_t stream) {
     clear_error();
     HWKV_TRY(check_cache(L, c));
     HWKV_TRY(check_batch(L, c, layer, 1, n_seqs, seq_slots));
@@ -418,6 +445,16 @@ static hwkv_status prefill_entry(const hwkv_layout* L, const hwkv_cache* c, int3
     if (out_dtype != HWKV_F32 && out_dtype != HWKV_BF16 && out_dtype != HWKV_F16)
         return fail(HWKV_ERR_INVALID_ARG, "out_dtype must be HWKV_F32, HWKV_BF16 or HWKV_F16");
     HWKV_TRY(check_scale(scale));
+    uint64_t need = 0;
+    if (!exact_p) {
+        HWKV_TRY(hwkv_prefill_workspace_bytes(L, layer, n_seqs, n_chunk, &need));
+        if (need > 0 && !ws) return fail(HWKV_ERR_INVALID_ARG, "null workspace");
+        if (ws && !aligned(ws, 256))
+            return fail(HWKV_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(HWKV_ERR_CAPACITY, "prefill workspace of " + std::to_string(ws_bytes) +
+                                               " bytes, need " + std::to_string(need));
+    }
     PrefillArgs a{};
     a.pool = static_cast<const uint8_t*>(c->pool);
     a.n_pool_blocks = pool_blocks(L, c);
@@ -445,16 +482,20 @@ static hwkv_status prefill_entry(const hwkv_layout* L, const hwkv_cache* c, int3
     while ((16 << a.tpb_log2) < L->block_size) a.tpb_log2++;
     a.exact_p = exact_p ? 1 : 0;
     a.qk_scale_log2 = scale * 1.4426950408889634f;
+    if (need > 0) {
+        a.v16 = static_cast<uint8_t*>(ws);
+        a.v16_seq_rows = prefill_v16_rows(*L, layer, n_chunk);
+    }
     return launch_prefill(*L, group, a, stream);
 }
 
 hwkv_status hwkv_prefill_attn(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
                               int32_t n_seqs, const int32_t* seq_slots, const int64_t* pos0,
                               int32_t n_chunk, int32_t n_q_heads, const void* q, const void* k,
-                              const void* v, void* out, hwkv_dtype out_dtype, float scale,
-                              hipStream_t stream) {
-    return prefill_entry(L, c, layer, n_seqs, seq_slots, pos0, n_chunk, n_q_heads, q, k, v, out,
-                         out_dtype, scale, false, stream);
+                              const void* v, void* ws, uint64_t ws_bytes, void* out,
+                              hwkv_dtype out_dtype, float scale, hipStream_t stream) {
+    return prefill_entry(L, c, layer, n_seqs, seq_slots, pos0, n_chunk, n_q_heads, q, k, v, ws,
+                         ws_bytes, out, out_dtype, scale, false, stream);
 }
 
 hwkv_status hwkv_prefill_attn_exact(const hwkv_layout* L, const hwkv_cache* c, int32_t layer,
@@ -462,8 +503,8 @@ hwkv_status hwkv_prefill_attn_exact(const hwkv_layout* L, const hwkv_cache* c, i
                                     const int64_t* pos0, int32_t n_chunk, int32_t n_q_heads,
                                     const void* q, const void* k, const void* v, void* out,
                                     hwkv_dtype out_dtype, float scale, hipStream_t stream) {
-    return prefill_entry(L, c, layer, n_seqs, seq_slots, pos0, n_chunk, n_q_heads, q, k, v, out,
-                         out_dtype, scale, true, stream);
+    return prefill_entry(L, c, layer, n_seqs, seq_slots, pos0, n_chunk, n_q_heads, q, k, v,
+                         nullptr, 0, out, out_dtype, scale, true, stream);
 }
 
 }  // extern "C"

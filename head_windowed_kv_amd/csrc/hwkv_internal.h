@@ -200,7 +200,21 @@ struct PrefillArgs {
     int32_t tpb_log2;  // log2(block_size / 16)
     int32_t exact_p;   // bf16 caches: P split into two bf16 products, no fp16 pass
     float qk_scale_log2;
+    // bf16 caches, fp16 pass: the workspace holding, per (sequence, kv head),
+    // fp16 copies of the V rows of keys [P - w + 1, P + n_chunk) (w - 1 + n_chunk
+    // rows, heads in order); v16_seq_rows = rows per sequence
+    uint8_t* v16;
+    int64_t v16_seq_rows;
 };
+
+// Rows of the fp16 V copy one sequence of a prefill call needs:
+// sum over the layer's kv heads of (w_h - 1 + n_chunk).
+inline int64_t prefill_v16_rows(const hwkv_layout& lay, int32_t layer, int32_t n_chunk) {
+    int64_t rows = 0;
+    for (int32_t h = 0; h < lay.n_kv_heads; h++)
+        rows += (int64_t)lay.windows[(size_t)layer * lay.n_kv_heads + h] - 1 + n_chunk;
+    return rows;
+}
 
 // Device address of the library's static decode scratch (the records of
 // hwkv_decode_append_attn_static) on the device that `stream` runs on: a

@@ -22,12 +22,14 @@
 // P rounded to bf16 alone costs ~3e-3 relative error on near-uniform softmax
 // rows, so the PV product takes P in fp16 (11 significant bits, 8x more
 // accurate) on v_mfma_f32_32x32x16_f16.  fp16 caches hold V in fp16 already;
-// for bf16 caches each wave converts its own slice of every V tile in LDS
-// after the slice's DMA lands (exact for |v| in fp16's normal range), and a
-// workgroup whose result shows a value outside that range (a non-finite or
-// a very small output row) runs again on the stored bf16 tiles with P split
-// into a bf16 high part and a bf16 remainder (two MFMAs).  That exact form is
-// also what hwkv_prefill_attn_exact runs directly.
+// for bf16 caches a pre-pass converts, once per call, the V rows each
+// (sequence, kv head) needs (keys [P - w + 1, P + n)) into an fp16 copy in the
+// caller's workspace (exact for |v| in fp16's normal range), and the fast pass
+// stages its V tiles from that copy; a row whose result shows a value outside
+// that range (non-finite, or very small) is marked and recomputed on the
+// stored bf16 tiles with P split into a bf16 high part and a bf16 remainder
+// (two MFMAs).  That exact form is also what hwkv_prefill_attn_exact runs
+// directly.
 //
 // head_dim 256: the accumulators and query operands take twice the registers
 // (484 VGPRs), so that instance runs one wave per SIMD, with 32 KiB tiles.
@@ -187,6 +189,9 @@ constexpr int kFast = 0, kExact = 1, kRedo = 2;
 template <int KT, int D, int G, bool BIG, int PASS>
 __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(PrefillArgs a) {
     static_assert(KT == kBF16 || PASS == kFast, "fp16 caches have a single pass");
+    // the fp16 pass on a bf16 cache reads its V tiles, already in fp16, from
+    // the copy the pre-pass wrote; every other pass reads the cache's own V
+    constexpr bool V16 = PASS == kFast && KT == kBF16;
     typedef PfCfg<D> C;
     // two stages of K and V tiles; separate objects so that the compiler sees
     // that a DMA into one stage never aliases the reads of the other
@@ -360,6 +365,35 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             }
         }
     };
+    // V16: key t of this (sequence, kv head) is row t - v16_first of its
+    // region of the fp16 copy (rows [0, w - 1 + n), fewer than 2^31 bytes);
+    // keys before the region (a tile that starts before the window) and past
+    // it get offsets beyond the buffer range and read as zero
+    const uint8_t* v16_base = nullptr;
+    uint32_t v16_bytes = 0;
+    int64_t v16_first = 0;
+    if constexpr (V16) {
+        int64_t off = 0;
+        for (int h = 0; h < kvh; h++)
+            off += (int64_t)a.heads[(int64_t)a.layer * a.n_kv_heads + h].window - 1 + n;
+        v16_base = a.v16 + ((int64_t)b * a.v16_seq_rows + off) * C::ROW;
+        v16_bytes = seq_ok ? (uint32_t)((w - 1 + n) * C::ROW) : 0u;
+        v16_first = P - (w - 1);
+    }
+    auto issue_v16 = [&](uint8_t* slot_base, int64_t X) {
+        uint8_t* dst = slot_base + wave * (kBS * C::ROW);
+        const int64_t tb = X * kBK + wave * kBS;  // first key of the slice
+        const rsrc_t r16 = make_rsrc(v16_base, v16_bytes);
+        // the whole offset in the range-checked operand (the scalar offset is
+        // not checked against the range)
+#pragma unroll
+        for (int j = 0; j < C::NI; j++) {
+            const int64_t i = tb + C::RPI * j + lq - v16_first;  // row of this lane's chunk
+            const uint32_t off = i >= 0 ? (uint32_t)(i * C::ROW) + (cv ^ xv(j)) : 0x80000000u;
+            dma16(r16, off, 0, dst + j * 1024);
+        }
+    };
+
     // ring block of the next slice's id: slice u_next lives in block
     // (u_next >> tpb_log2) % nb; successive tiles advance u by kBK / kBS
     uint32_t u_next = (uint32_t)(T0 * (kBK / kBS) + wave);  // positions < 2^35
@@ -487,7 +521,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     };
 
     // O^T += V^T P^T for k-step ks; the V^T operands come from transpose reads
-    // (fp16 when F16P: an fp16 cache, or a bf16 tile converted in LDS)
+    // (fp16 when F16P: an fp16 cache, or the pre-pass's fp16 copy of a bf16 cache)
     auto pv = [&](auto f16p_tag, const uint8_t* vt, int ks, const u32x4& hi, const u32x4& lo) {
         constexpr bool F16P = decltype(f16p_tag)::value;
         const int roff = ((ks >> 1) * 32 + (ks & 1) * 16) * C::ROW;
@@ -509,39 +543,21 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         }
     };
 
-    // bf16 -> fp16 in place over this wave's 16-key slice of a V tile (the
-    // slice its own DMA filled).  Exact while |v| lies in fp16's normal
-    // range; values outside it are caught by the check after the key loop.
-    auto slice_to_f16 = [&](uint8_t* vbuf) {
-        uint8_t* base = vbuf + wave * (kBS * C::ROW) + lane * 16;
-        u32x4 x[C::NI];
-#pragma unroll
-        for (int j = 0; j < C::NI; j++) x[j] = *reinterpret_cast<const u32x4*>(base + j * 1024);
-#pragma unroll
-        for (int j = 0; j < C::NI; j++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t w2 = x[j][e];
-                x[j][e] = pack_f16(__uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u));
-            }
-#pragma unroll
-        for (int j = 0; j < C::NI; j++) *reinterpret_cast<u32x4*>(base + j * 1024) = x[j];
-    };
-
     // ---- software pipeline over key tiles ----
     // Iteration it (tile T = T0 + it) finds S^T of T in registers and K of
-    // T + 1, V of T in LDS; it starts the DMA of V of T + 1 and K of T + 2,
+    // T + 1, V of T in LDS; it starts the DMA of K of T + 2 and V of T + 1,
     // computes S^T of T + 1 while it exponentiates T, and multiplies P of T
-    // into O while it finishes the exponentials and masks T + 1.  When V is
-    // converted to fp16, each wave converts its slice of V of T + 1 at the
-    // end of the iteration (waiting for its own DMA of it only); the next
-    // iteration's barrier publishes the slice to the other waves.
+    // into O while it finishes the exponentials and masks T + 1.
     f32x16 sA[2], sB[2];  // S^T of the current and of the next tile, alternating
     float mt = kEmptyMax;
     int32_t idK = 0, idV = 0;
+    auto issue_vt = [&](uint8_t* slot_base, int64_t X, int32_t id) {
+        if constexpr (V16)
+            issue_v16(slot_base, X);
+        else
+            issue(slot_base, X, id, true);
+    };
     auto run = [&](auto f16p_tag) {
-        constexpr bool F16P = decltype(f16p_tag)::value;
-        constexpr bool CONV = F16P && KT == kBF16;
         u_next = (uint32_t)(T0 * (kBK / kBS) + wave);
         jw = (int32_t)((u_next >> tpb_log2) % (uint32_t)nb);
         m_run = kEmptyMax;
@@ -552,33 +568,19 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         if (n_tiles > 0) {
             const int32_t id0 = next_id();
             issue(sK0, T0, id0, false);
-            issue(sV0, T0, id0, true);
+            issue_vt(sV0, T0, id0);
             const int32_t id1 = next_id();
             if (n_tiles > 1) issue(sK1, T0 + 1, id1, false);
             idV = id1;
             idK = next_id();
         }
         __builtin_amdgcn_s_waitcnt(0);
-        if (CONV && n_tiles > 0) {
-            __asm__ volatile("" ::: "memory");
-            slice_to_f16(sV0);
-        }
         __syncthreads();
         if (wave_on && n_tiles > 0) {
             qk(sK0, sA[0], sA[1]);
             mt = mask_max(sA, T0);
         }
 
-        // this wave's DMA of V of T + 1 has landed (the K DMA issued after
-        // it may still be in flight)
-        auto convert_next_v = [&](int it, uint8_t* v_dma) {
-            if (it + 2 < n_tiles)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm<C::NI>());
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-            __asm__ volatile("" ::: "memory");
-            slice_to_f16(v_dma);
-        };
         auto step = [&](int it, const uint8_t* k_rd, const uint8_t* v_rd, uint8_t* k_dma,
                         uint8_t* v_dma, f32x16* s_cur, f32x16* s_next) {
             const int64_t T = T0 + it;
@@ -587,19 +589,11 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             // are free
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if constexpr (CONV) {  // V first: its wait below leaves the K DMA in flight
-                if (it + 1 < n_tiles) issue(v_dma, T + 1, idV, true);
-                if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
-            } else {
-                if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
-                if (it + 1 < n_tiles) issue(v_dma, T + 1, idV, true);
-            }
+            if (it + 2 < n_tiles) issue(k_dma, T + 2, idK, false);
+            if (it + 1 < n_tiles) issue_vt(v_dma, T + 1, idV);
             idV = idK;
             idK = next_id();
-            if (!wave_on) {
-                if (CONV && it + 1 < n_tiles) convert_next_v(it, v_dma);
-                return;
-            }
+            if (!wave_on) return;
             if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
                 const float m_new = fmaxf(m_run, mt);
                 const float alpha = fast_exp2(m_run - m_new);
@@ -623,7 +617,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             pv(f16p_tag, v_rd, 3, phi[3], plo[3]);
             l_run += psum;
             if (it + 1 < n_tiles) mt = mask_max(s_next, T + 1);
-            if (CONV && it + 1 < n_tiles) convert_next_v(it, v_dma);
         };
         for (int it = 0; it < n_tiles; it += 2) {
             step(it, sK1, sV0, sK0, sV1, sA, sB);
@@ -633,7 +626,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     };
 
     if constexpr (PASS == kFast)
-        run(BoolC<true>{});  // P in fp16 (bf16 caches: V converted to fp16 in LDS)
+        run(BoolC<true>{});  // P in fp16, V in fp16 (bf16 caches: from the pre-pass copy)
     else
         run(BoolC<false>{});  // P as a truncated bf16 part and a bf16 remainder
 
@@ -690,6 +683,90 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         }
 }
 
+// Pre-pass of the fp16 pass on bf16 caches: the fp16 copy of the V rows of
+// keys [P - w + 1, P + n) of every (sequence, kv head), keys before P from the
+// cache's ring, keys from P on from the chunk's v, rounded to nearest even
+// (exact for |v| in fp16's normal range; a value beyond it becomes inf, which
+// the fast pass's row check catches).  A key held by a block outside the pool
+// gets zeros (its rows come out NaN by the lost-key rule of the main pass);
+// keys below 0 and sequences with a bad slot or position are not written
+// (never staged).  Grid: x = (sequence, kv head), y strides over the 16-byte
+// chunks of its rows.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_v16_kernel(PrefillArgs a) {
+    typedef PfCfg<D> C;
+    const int pair = blockIdx.x;
+    const int b = pair / a.n_kv_heads, h = pair % a.n_kv_heads;
+    const uint64_t fp = *reinterpret_cast<const uint64_t*>(a.meta + 8);
+    if (fp != a.fingerprint) return;
+    const int64_t P = a.pos0[b];
+    const int64_t slot = a.seq_slots ? (int64_t)a.seq_slots[b] : (int64_t)b;
+    if (P < 0 || slot < 0 || slot >= a.table_rows) return;
+    const HeadDesc* hl = a.heads + (int64_t)a.layer * a.n_kv_heads;
+    const HeadDesc hd = hl[h];
+    const int n = a.n_chunk;
+    int64_t off = 0;
+    for (int i = 0; i < h; i++) off += (int64_t)hl[i].window - 1 + n;
+    uint8_t* dst0 = a.v16 + ((int64_t)b * a.v16_seq_rows + off) * C::ROW;
+    const int64_t rows = (int64_t)hd.window - 1 + n, first = P - (hd.window - 1);
+    const int32_t* tbl = a.block_ids + slot * a.blocks_per_seq + hd.table_off;
+    const int lbs = 4 + a.tpb_log2;  // log2 of the block size
+    const uint32_t nb = (uint32_t)hd.nblocks;
+    const uint8_t* vbase = a.v + (int64_t)h * C::ROW + (int64_t)b * n * a.n_kv_heads * C::ROW;
+    const int64_t crow = (int64_t)a.n_kv_heads * C::ROW;  // bytes between chunk rows
+    // U chunks per thread in flight: loads first, then conversions and stores
+    constexpr int U = 4;
+    const uint64_t n_el = (uint64_t)rows * C::CPR;
+    for (uint64_t e0 = (uint64_t)blockIdx.y * (256 * U) + threadIdx.x; e0 < n_el;
+         e0 += (uint64_t)gridDim.y * (256 * U)) {
+        u32x4 x[U];
+        bool keep[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t e = e0 + (uint64_t)u * 256;
+            const int64_t i = (int64_t)(e / C::CPR);
+            const int c = (int)(e % C::CPR);
+            const int64_t t = first + i;
+            keep[u] = e < n_el && t >= 0;
+            x[u] = u32x4{0u, 0u, 0u, 0u};
+            if (!keep[u]) continue;
+            if (t < P) {
+                const int32_t id = tbl[(uint32_t)(t >> lbs) % nb];
+                if (id >= 0 && (uint64_t)id < a.n_pool_blocks)
+                    x[u] = *reinterpret_cast<const u32x4*>(
+                        a.pool + (uint64_t)id * a.block_bytes +
+                        (((int64_t)1 << lbs) + (t & (((int64_t)1 << lbs) - 1))) * C::ROW + c * 16);
+            } else {
+                x[u] = *reinterpret_cast<const u32x4*>(vbase + (t - P) * crow + c * 16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (!keep[u]) continue;
+            const uint64_t e = e0 + (uint64_t)u * 256;
+            u32x4 y;
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                y[k] = pack_f16(__uint_as_float(x[u][k] << 16),
+                                __uint_as_float(x[u][k] & 0xffff0000u));
+            *reinterpret_cast<u32x4*>(dst0 + e * 16) = y;
+        }
+    }
+}
+
+template <int D>
+hwkv_status launch_v16(const PrefillArgs& a, hipStream_t s) {
+    // about 2048 workgroups over the whole grid, at most 256 per pair
+    const int64_t pairs = (int64_t)a.n_seqs * a.n_kv_heads;
+    const int64_t per = (2048 + pairs - 1) / pairs;
+    dim3 grid((unsigned)pairs, (unsigned)(per < 256 ? per : 256));
+    hipLaunchKernelGGL(prefill_v16_kernel<D>, grid, dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(HWKV_ERR_HIP, std::string("prefill pre-pass launch: ") + hipGetErrorString(e));
+    return HWKV_OK;
+}
+
 template <int T, int D, int G, bool BIG>
 hwkv_status launch_pass(const PrefillArgs& a, int pass, hipStream_t s) {
     auto kernel = prefill_kernel<T, D, G, BIG, kFast>;
@@ -711,13 +788,17 @@ hwkv_status launch_pass(const PrefillArgs& a, int pass, hipStream_t s) {
     return HWKV_OK;
 }
 
-// bf16 caches: the exact entry runs kExact; the default entry runs kFast and
-// then kRedo (which exits at once unless a workgroup needs the exact pass).
-// fp16 caches: one kFast launch.
+// bf16 caches: the exact entry runs kExact; the default entry runs the V
+// pre-pass, kFast, and then kRedo (which exits at once unless a workgroup
+// holds a marked row).  fp16 caches: one kFast launch.
 template <int T, int D, int G>
 hwkv_status launch_t(const PrefillArgs& a, hipStream_t s) {
     auto run = a.tpb_log2 > 0 ? launch_pass<T, D, G, true> : launch_pass<T, D, G, false>;
     if (T == kBF16 && a.exact_p) return run(a, kExact, s);
+    if (T == kBF16) {
+        const hwkv_status st = launch_v16<D>(a, s);
+        if (st != HWKV_OK) return st;
+    }
     const hwkv_status st = run(a, kFast, s);
     if (st != HWKV_OK || T != kBF16) return st;
     return run(a, kRedo, s);

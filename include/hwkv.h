@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define HWKV_ABI_VERSION 2u
+#define HWKV_ABI_VERSION 3u
 
 typedef enum hwkv_status {
     HWKV_OK = 0,
@@ -372,6 +372,19 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
                              uint64_t workspace_bytes, void *out, hwkv_dtype out_dtype,
                              hipStream_t stream);
 
+/* Device workspace of hwkv_prefill_attn for layer `layer`, n_seqs sequences
+ * and chunks of n_chunk rows.  BF16 caches: the fp16 copy of the V rows the
+ * call reads, w - 1 + n_chunk rows of head_dim fp16 values per (sequence, kv
+ * head), heads in order, sequences in order.  F16 and F32 caches need none
+ * (0 bytes).  The pages give no prefill kernel; this buffer belongs to this
+ * library's form of it (see hwkv_prefill_attn).  HWKV_ERR_UNSUPPORTED when one
+ * head's rows would take 2^31 bytes or more (hwkv_prefill_attn_exact needs no
+ * workspace); HWKV_ERR_INVALID_ARG for a layer out of range, n_seqs < 1 or
+ * n_chunk < 1. */
+hwkv_status hwkv_prefill_workspace_bytes(const hwkv_layout *layout, int32_t layer,
+                                         int32_t n_seqs, int32_t n_chunk,
+                                         uint64_t *bytes);
+
 /* Chunked prefill of one layer.  The pages define the per-head window (摘要,
  * 核心技术 2; "KV Cache Consistency Practices ...", "SWA Window") but no
  * prefill kernel: this is the same windowed attention for a chunk of new
@@ -382,7 +395,10 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  * w-1 of them can be needed, and the ring holds at least w), keys from P on
  * from k, v.  q: device [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: device
  * [n_seqs][n_chunk][n_kv_heads][head_dim]; out: [n_seqs][n_chunk][n_q_heads]
- * [head_dim] as out_dtype (F32, BF16 or F16).  The cache is read, not written: call hwkv_append
+ * [head_dim] as out_dtype (F32, BF16 or F16).  workspace: device memory of
+ * hwkv_prefill_workspace_bytes (256-byte aligned; null allowed when that is
+ * 0), scratch of this call only: its contents on return mean nothing, and
+ * two calls in flight on one workspace race.  The cache is read, not written: call hwkv_append
  * with the same k, v (n_layers = 1) afterwards, since appending first could
  * overwrite history that earlier rows of the chunk still need.  Runs on
  * MFMA tiles (bf16 or fp16 operands, fp32 accumulation).  scale: finite
@@ -391,30 +407,33 @@ hwkv_status hwkv_decode_step(const hwkv_layout *layout, const hwkv_cache *cache,
  *
  * Precision of the softmax weights P in the P.V product: they are rounded
  * once to fp16 (11 significant bits; row error a few 1e-4 of the row's
- * largest output on N(0,1) data).  For BF16 caches this needs V in fp16:
- * each V tile is converted in on-chip memory, which is exact for |v| in
- * [2^-14, 65504].  A query row whose result comes out non-finite (a V
- * element beyond fp16's range) or whose largest magnitude is below 2^-12 of
- * its softmax sum (where the conversion's absolute error, at most 2^-25 per
- * element, could matter) is recomputed as hwkv_prefill_attn_exact does, so
- * such inputs cost time, not accuracy.  For BF16 caches the call enqueues two
- * kernels: the fp16 pass, which writes such rows as NaN, and a second pass
- * that exits at once unless a row of its workgroup is NaN, in which case it
- * recomputes the workgroup exactly and rewrites those rows (rows that are NaN
- * by the rules above come out NaN again). */
+ * largest output on N(0,1) data).  For BF16 caches this needs V in fp16: a
+ * first kernel writes the fp16 copy of the V rows the call reads into the
+ * workspace (rounded to nearest even, exact for |v| in [2^-14, 65504]).  A
+ * query row whose result comes out non-finite (a V element beyond fp16's
+ * range) or whose largest magnitude is below 2^-12 of its softmax sum (where
+ * the conversion's absolute error, at most 2^-25 per element, could matter)
+ * is recomputed as hwkv_prefill_attn_exact does, from the cache's bf16 V, so
+ * such inputs cost time, not accuracy.  For BF16 caches the call enqueues
+ * three kernels: the fp16 copy, the fp16 pass, which writes such rows as NaN,
+ * and a second pass that exits at once unless a row of its workgroup is NaN,
+ * in which case it recomputes the workgroup exactly and rewrites those rows
+ * (rows that are NaN by the rules above come out NaN again). */
 hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer, int32_t n_seqs,
                               const int32_t *seq_slots, const int64_t *pos0,
                               int32_t n_chunk, int32_t n_q_heads, const void *q,
-                              const void *k, const void *v, void *out,
+                              const void *k, const void *v, void *workspace,
+                              uint64_t workspace_bytes, void *out,
                               hwkv_dtype out_dtype, float scale,
                               hipStream_t stream);
 
 /* hwkv_prefill_attn with the P.V product at ~16-bit precision for BF16
  * caches: P is split into its truncation to bf16 and the remainder rounded
  * to bf16, two bf16 products (row error ~1e-5 of the row's largest output),
- * at about 10% more time.  For F16 caches it is hwkv_prefill_attn.  Same
- * arguments, layouts and errors. */
+ * at about 10% more time; one kernel, no workspace.  For F16 caches it is
+ * hwkv_prefill_attn.  Same arguments (without the workspace), layouts and
+ * errors. */
 hwkv_status hwkv_prefill_attn_exact(const hwkv_layout *layout,
                                     const hwkv_cache *cache, int32_t layer,
                                     int32_t n_seqs, const int32_t *seq_slots,

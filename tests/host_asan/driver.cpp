@@ -85,6 +85,19 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
     EXPECT(hwkv_workspace_bytes(lay, 0, L + 1, (int32_t)n_seqs, nq, &ws) != HWKV_OK);
     EXPECT(hwkv_workspace_bytes(lay, 0, L, (int32_t)n_seqs, nq + 1, &ws) != HWKV_OK);
     EXPECT(hwkv_step_workspace_bytes(lay, 0, L, (int32_t)n_seqs, nq, &sws) == HWKV_OK);
+    // prefill: bf16 caches take an fp16 copy of the V rows, other dtypes none
+    uint64_t pws = 1, pws7 = 1;
+    EXPECT(hwkv_prefill_workspace_bytes(lay, L - 1, (int32_t)n_seqs, 77, &pws) == HWKV_OK);
+    EXPECT(hwkv_prefill_workspace_bytes(lay, 0, (int32_t)n_seqs, 7, &pws7) == HWKV_OK);
+    {
+        uint64_t rows = 0;
+        for (int h = 0; h < H; h++) rows += (uint64_t)w[(size_t)(L - 1) * H + h] - 1 + 77;
+        EXPECT(pws == (dt == HWKV_BF16 ? (uint64_t)n_seqs * rows * (uint64_t)d * 2 : 0));
+    }
+    EXPECT(hwkv_prefill_workspace_bytes(lay, L, (int32_t)n_seqs, 7, &pws7) != HWKV_OK);
+    EXPECT(hwkv_prefill_workspace_bytes(lay, 0, (int32_t)n_seqs, 0, &pws7) != HWKV_OK);
+    EXPECT(hwkv_prefill_workspace_bytes(lay, 0, (int32_t)n_seqs, 7, nullptr) != HWKV_OK);
+    EXPECT(hwkv_prefill_workspace_bytes(lay, 0, (int32_t)n_seqs, 7, &pws7) == HWKV_OK);
 
     uint64_t mfp = 0;
     EXPECT(hwkv_meta_fingerprint(meta.data(), meta.size(), &mfp) == HWKV_OK);
@@ -125,8 +138,8 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
     if (ws <= HWKV_STATIC_SCRATCH_BYTES)
         EXPECT(hwkv_decode_append_attn_static(lay, &c, 0, L, ns, slots, pos, k, v, nq, q, 0.1f,
                                               out, HWKV_BF16, nullptr) == HWKV_OK);
-    EXPECT(hwkv_prefill_attn(lay, &c, L - 1, ns, slots, pos, 77, nq, q, k, v, out, HWKV_BF16,
-                             0.1f, nullptr) == HWKV_OK);
+    EXPECT(hwkv_prefill_attn(lay, &c, L - 1, ns, slots, pos, 77, nq, q, k, v, wsp, pws, out,
+                             HWKV_BF16, 0.1f, nullptr) == HWKV_OK);
     EXPECT(hwkv_prefill_attn_exact(lay, &c, 0, ns, nullptr, pos, 1, nq, q, k, v, out, HWKV_F32,
                                    0.1f, nullptr) == HWKV_OK);
     // the merge reads only the workspace and the contexts: a batch larger
@@ -152,12 +165,18 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
                             out, HWKV_F32, nullptr) == HWKV_ERR_MISALIGNED);
     EXPECT(hwkv_decode_step(lay, &c, 0, L, ns, slots, pos, k, v, nq, q, 0.1f, wsp, ws - 1, out,
                             HWKV_F32, nullptr) != HWKV_OK);
-    EXPECT(hwkv_prefill_attn(lay, &c, L, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, 0.1f,
-                             nullptr) != HWKV_OK);
+    EXPECT(hwkv_prefill_attn(lay, &c, L, ns, slots, pos, 7, nq, q, k, v, wsp, pws7, out,
+                             HWKV_F32, 0.1f, nullptr) != HWKV_OK);
+    if (pws7 > 0) {  // a short or missing prefill workspace
+        EXPECT(hwkv_prefill_attn(lay, &c, 0, ns, slots, pos, 7, nq, q, k, v, wsp, pws7 - 1, out,
+                                 HWKV_F32, 0.1f, nullptr) == HWKV_ERR_CAPACITY);
+        EXPECT(hwkv_prefill_attn(lay, &c, 0, ns, slots, pos, 7, nq, q, k, v, nullptr, pws7, out,
+                                 HWKV_F32, 0.1f, nullptr) == HWKV_ERR_INVALID_ARG);
+    }
     EXPECT(hwkv_prefill_attn_exact(lay, &c, 0, ns, slots, pos, 0, nq, q, k, v, out, HWKV_F32,
                                    0.1f, nullptr) != HWKV_OK);
-    EXPECT(hwkv_prefill_attn(lay, nullptr, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, 0.1f,
-                             nullptr) != HWKV_OK);
+    EXPECT(hwkv_prefill_attn(lay, nullptr, 0, ns, slots, pos, 7, nq, q, k, v, wsp, pws7, out,
+                             HWKV_F32, 0.1f, nullptr) != HWKV_OK);
     // the static scratch refuses a call whose records exceed it
     EXPECT(hwkv_decode_append_attn_static(lay, &c, 0, L, 65535, slots, pos, k, v, nq, q, 0.1f,
                                           out, HWKV_F32, nullptr) == HWKV_ERR_CAPACITY);
@@ -173,8 +192,8 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
            HWKV_ERR_ABI_MISMATCH);
     EXPECT(hwkv_decode_step(lay, &other, 0, L, ns, slots, pos, k, v, nq, q, 0.1f, wsp, sws, out,
                             HWKV_F32, nullptr) == HWKV_ERR_ABI_MISMATCH);
-    EXPECT(hwkv_prefill_attn(lay, &other, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, 0.1f,
-                             nullptr) == HWKV_ERR_ABI_MISMATCH);
+    EXPECT(hwkv_prefill_attn(lay, &other, 0, ns, slots, pos, 7, nq, q, k, v, wsp, pws7, out,
+                             HWKV_F32, 0.1f, nullptr) == HWKV_ERR_ABI_MISMATCH);
     // the softmax scale must be finite and positive
     const float bad_scales[3] = {0.0f, -0.5f, __builtin_nanf("")};
     for (float sc : bad_scales) {
@@ -182,8 +201,8 @@ static void exercise(int L, int H, const std::vector<int32_t>& w, int bs, int d,
                                 nullptr) == HWKV_ERR_INVALID_ARG);
         EXPECT(hwkv_decode_step(lay, &c, 0, L, ns, slots, pos, k, v, nq, q, sc, wsp, sws, out,
                                 HWKV_F32, nullptr) == HWKV_ERR_INVALID_ARG);
-        EXPECT(hwkv_prefill_attn(lay, &c, 0, ns, slots, pos, 7, nq, q, k, v, out, HWKV_F32, sc,
-                                 nullptr) == HWKV_ERR_INVALID_ARG);
+        EXPECT(hwkv_prefill_attn(lay, &c, 0, ns, slots, pos, 7, nq, q, k, v, wsp, pws7, out,
+                                 HWKV_F32, sc, nullptr) == HWKV_ERR_INVALID_ARG);
     }
     EXPECT(hwkv::g_launches == mid);
     hwkv_layout_destroy(lay);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version():
     # 2: hwkv_cache carries the fingerprint of its meta blob
-    assert hw.hwkv_abi_version() == hw.ABI_VERSION == 2
+    assert hw.hwkv_abi_version() == hw.ABI_VERSION == 3
     text = open(os.path.join(ROOT, "include", "hwkv.h")).read()
     assert re.search(r"#define HWKV_ABI_VERSION %du\b" % hw.ABI_VERSION, text)
 
@@ -97,6 +97,53 @@ def test_workspace_bytes():
     assert hw.hwkv_workspace_bytes(lay, 0, 2, 5, 6) == 12 * 392 * 4 * 5
     assert hw.hwkv_workspace_bytes(lay, 1, 1, 1, 6) == 2 * 392 * 4
     assert hw.hwkv_workspace_bytes(lay, 0, 1, 1, 2) == 10 * 132 * 4
+
+
+def test_prefill_workspace_bytes():
+    """bf16 caches: one fp16 V row of head_dim values per key of
+    [P - w + 1, P + n_chunk), per (sequence, kv head); other dtypes: none."""
+    w = np.array([[64, 700], [1, 4096]], np.int32)
+    lay = hw.hwkv_layout_create(w, 16, 128, "bf16")
+    assert hw.hwkv_prefill_workspace_bytes(lay, 0, 3, 40) == 3 * ((63 + 40) + (699 + 40)) * 256
+    assert hw.hwkv_prefill_workspace_bytes(lay, 1, 1, 1) == (1 + 4096) * 256
+    for dt in ("f16", "f32"):
+        lay16 = hw.hwkv_layout_create(w, 16, 64, dt)
+        assert hw.hwkv_prefill_workspace_bytes(lay16, 1, 8, 2048) == 0
+    for args in ((2, 1, 1), (-1, 1, 1), (0, 0, 1), (0, 1, 0)):
+        with pytest.raises(hw.HwkvError) as e:
+            hw.hwkv_prefill_workspace_bytes(lay, *args)
+        assert e.value.status_name == "HWKV_ERR_INVALID_ARG", args
+    # one head's rows reach 2^31 bytes (d = 128: 2^23 rows of 256 bytes)
+    big = hw.hwkv_layout_create([[(1 << 23) - 100, 16]], 16, 128, "bf16")
+    assert hw.hwkv_prefill_workspace_bytes(big, 0, 1, 100) == ((1 << 23) - 1 + 15 + 100) * 256
+    with pytest.raises(hw.HwkvError) as e:
+        hw.hwkv_prefill_workspace_bytes(big, 0, 1, 101)
+    assert e.value.status_name == "HWKV_ERR_UNSUPPORTED"
+    assert "hwkv_prefill_attn_exact" in str(e.value)
+
+
+def test_prefill_workspace_errors_before_launch():
+    """A missing, misaligned or short prefill workspace is refused on the
+    host; the exact entry takes none."""
+    lay = hw.hwkv_layout_create([[64, 700]], 16, 128, "bf16")
+    cv = _fake_cache(lay, hw.hwkv_mem_estimate(lay, 2), 2)
+    P = lambda mib: ctypes.c_void_p(mib << 20)  # noqa: E731
+    need = hw.hwkv_prefill_workspace_bytes(lay, 0, 2, 40)
+
+    def call(ws, nbytes):
+        return hw.STATUS_NAMES[hw._lib.hwkv_prefill_attn(
+            lay.handle, ctypes.byref(cv), 0, 2, None, P(10), 40, 6, P(9), P(5), P(6), ws, nbytes,
+            P(11), 0, 0.1, None)]
+
+    assert call(None, need) == "HWKV_ERR_INVALID_ARG"
+    assert call(ctypes.c_void_p((8 << 20) + 16), need) == "HWKV_ERR_MISALIGNED"
+    assert call(P(8), need - 1) == "HWKV_ERR_CAPACITY"
+    assert "need %d" % need in hw.hwkv_last_error()
+    big = hw.hwkv_layout_create([[(1 << 23) - 100, 16]], 16, 128, "bf16")
+    cvb = _fake_cache(big, hw.hwkv_mem_estimate(big, 1), 1)
+    st = hw._lib.hwkv_prefill_attn(big.handle, ctypes.byref(cvb), 0, 1, None, P(10), 101, 2,
+                                   P(9), P(5), P(6), P(8), 1 << 40, P(11), 0, 0.1, None)
+    assert hw.STATUS_NAMES[st] == "HWKV_ERR_UNSUPPORTED"
 
 
 def test_meta_blob_header():
@@ -190,7 +237,8 @@ def _unsupported_calls(lay, group):
                                       p[3], float("inf"), ctypes.c_void_p(256 << 20), ws_bytes,
                                       p[4], 0, None)
     st_pf = hw._lib.hwkv_prefill_attn(lay.handle, ctypes.byref(cv), 0, 1, None, p[0], 0, n_q,
-                                      p[3], p[1], p[2], p[4], 0, 0.1, None)
+                                      p[3], p[1], p[2], ctypes.c_void_p(256 << 20), ws_bytes,
+                                      p[4], 0, 0.1, None)
     st_pfx = hw._lib.hwkv_prefill_attn_exact(lay.handle, ctypes.byref(cv), 0, 1, None, p[0], 0,
                                              n_q, p[3], p[1], p[2], p[4], 0, 0.1, None)
     assert st_pfx == st_pf  # the exact variant validates the same way
@@ -297,8 +345,8 @@ def _every_device_call(lay, cv, scale=0.1, n_q=4, with_scale_only=False):
                                   big, P(11), 0, None),
         L.hwkv_decode_step(h, c, 0, 1, 1, None, P(10), P(5), P(6), n_q, P(9), scale, P(8), big,
                            P(11), 0, None),
-        L.hwkv_prefill_attn(h, c, 0, 1, None, P(10), 7, n_q, P(9), P(5), P(6), P(11), 0, scale,
-                            None),
+        L.hwkv_prefill_attn(h, c, 0, 1, None, P(10), 7, n_q, P(9), P(5), P(6), P(8), big, P(11),
+                            0, scale, None),
         L.hwkv_prefill_attn_exact(h, c, 0, 1, None, P(10), 7, n_q, P(9), P(5), P(6), P(11), 0,
                                   scale, None),
     ]

@@ -124,10 +124,10 @@ def test_prefill_block_id_outside_the_pool_gives_nan_rows_that_reach_it():
     # to 437 + r, so rows 0..26 read them
     c.cache.block_ids[0, off[0] + (448 // 16) % 4] = -5
     torch.cuda.synchronize()
-    for name, fn in (("fast", H.hwkv_prefill_attn), ("exact", H.hwkv_prefill_attn_exact)):
+    for name in ("fast", "exact"):
         say("prefill bad id, entry", name)
         out = torch.zeros_like(want_good[name])
-        fn(c.cache, 0, torch.tensor(c.pos0, device=dev), c.q, c.k, c.v, out, scale)
+        c.call(torch.tensor(c.pos0, device=dev), out, scale, exact=name == "exact")
         torch.cuda.synchronize()
         nan = torch.isnan(out)
         want = torch.zeros(nan.shape[:3], dtype=torch.bool, device=dev)
@@ -187,9 +187,9 @@ def test_foreign_meta_blob_prefill(out_dtype):
     c = PrefillCase([64, 700], 128, 3, [500, 0], 77, seed=604)
     other = H.hwkv_layout_create([[64, 701]], 16, 128, torch.bfloat16)
     bad = _lying_cache(H, c.cache, other)
-    for fn in (H.hwkv_prefill_attn, H.hwkv_prefill_attn_exact):
+    for exact in (False, True):
         out = torch.zeros((2, 77, 6, 128), dtype=out_dtype, device=dev)
-        fn(bad, 0, torch.tensor(c.pos0, device=dev), c.q, c.k, c.v, out, 1.0 / math.sqrt(128))
+        c.call(torch.tensor(c.pos0, device=dev), out, 1.0 / math.sqrt(128), exact=exact, cache=bad)
         torch.cuda.synchronize()
         assert torch.all(torch.isnan(out.float()))
 

@@ -37,6 +37,10 @@ class PrefillCase:
         n_seqs = len(pos0)
         self.lay = H.hwkv_layout_create(self.windows[None, :], block_size, d, dtype)
         self.cache = H.make_cache(self.lay, n_seqs, device=dev, fill=0xFF, block_ids=block_ids)
+        # the fast entry's workspace, filled with NaN bit patterns: rows the
+        # call reads are always written first
+        self.ws = H.make_prefill_workspace(self.lay, 0, n_seqs, n, device=dev)
+        self.ws.fill_(0xFF)
         g = synth.gen(seed, dev)
         bs = block_size
         cap = int(((self.windows.astype(np.int64) + bs - 1) // bs * bs).max())
@@ -73,10 +77,20 @@ class PrefillCase:
         out = torch.full((len(self.pos0), self.n, self.n_kv * self.G, self.d), float("nan"),
                          dtype=out_dtype, device=dev)
         s = 1.0 / math.sqrt(self.d) if scale is None else scale
-        fn = H.hwkv_prefill_attn_exact if exact else H.hwkv_prefill_attn
-        fn(self.cache, 0, torch.tensor(self.pos0, device=dev), self.q, self.k, self.v, out, s)
+        self.call(torch.tensor(self.pos0, device=dev), out, s, exact=exact)
         torch.cuda.synchronize()
         return out
+
+    def call(self, pos0, out, scale, exact=False, seq_slots=None, cache=None):
+        """One call of the fast (default) or the exact entry on this case's q, k, v."""
+        H = hw()
+        cache = self.cache if cache is None else cache
+        if exact:
+            H.hwkv_prefill_attn_exact(cache, 0, pos0, self.q, self.k, self.v, out, scale,
+                                      seq_slots=seq_slots)
+        else:
+            H.hwkv_prefill_attn(cache, 0, pos0, self.q, self.k, self.v, self.ws, out, scale,
+                                seq_slots=seq_slots)
 
     def oracle(self, rows=None, scale=None):
         s = 1.0 / math.sqrt(self.d) if scale is None else scale
@@ -400,8 +414,8 @@ def test_prefill_graph_replays_match_eager():
     scale = 1.0 / math.sqrt(c.d)
 
     def calls():
-        H.hwkv_prefill_attn(c.cache, 0, pos, c.q, c.k, c.v, o_fast, scale)
-        H.hwkv_prefill_attn_exact(c.cache, 0, pos, c.q, c.k, c.v, o_exact, scale)
+        c.call(pos, o_fast, scale)
+        c.call(pos, o_exact, scale, exact=True)
 
     calls()
     torch.cuda.synchronize()
@@ -439,8 +453,8 @@ def test_invalid_slot_and_negative_position_give_nan_rows():
     for slots, pos0, bad in (([0, 7, 2], c.pos0, 1), ([0, 1, 2], [500, -3, 900], 1),
                              ([-1, 1, 2], c.pos0, 0)):
         out = torch.zeros_like(good)
-        H.hwkv_prefill_attn(c.cache, 0, torch.tensor(pos0, device=dev), c.q, c.k, c.v, out,
-                            scale, seq_slots=torch.tensor(slots, dtype=torch.int32, device=dev))
+        c.call(torch.tensor(pos0, device=dev), out, scale,
+               seq_slots=torch.tensor(slots, dtype=torch.int32, device=dev))
         torch.cuda.synchronize()
         assert torch.all(torch.isnan(out[bad])), (slots, pos0)
         for b in range(3):
