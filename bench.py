@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the 161K chunked-prefill leg (e.g. under rocprofv3 --pmc)")
+    p.add_argument("--single-layer-only", action="store_true",
+                   help="run only the one-layer, 8-sequence, 32K-context decode leg (e.g. "
+                        "under rocprofv3)")
     p.add_argument("--config", choices=("stack48", "cb"), default="stack48",
                    help="stack48: the 48-layer 112K decode step (default, the headline line); "
                         "cb: the 32-sequence continuous batch, 256 steps (138 GB pool)")
@@ -90,6 +93,10 @@ def load_traffic(split_tokens: int):
 
 
 PROBE_COPY_BYTES = 1 << 30
+# decode split length of the one-layer, 8-sequence, 32K leg: the fastest for
+# that workload in a sweep of 256-2048 tokens (0.1187 ms against 0.122 ms at
+# the default 1024)
+SINGLE_LAYER_SPLIT = 1536
 
 
 def probe_lib():
@@ -217,6 +224,15 @@ def main():
         import synth
         torch.cuda.set_device(0)
         print(json.dumps({"prefill_161k": prefill_leg(H, torch, synth)}), flush=True)
+        return
+    if args.single_layer_only:
+        import torch
+
+        import head_windowed_kv_amd as H
+        import synth
+        torch.cuda.set_device(0)
+        print(json.dumps({"single_layer_8seqs_ctx32k": single_layer_leg(
+            H, torch, synth, split_tokens=SINGLE_LAYER_SPLIT)}), flush=True)
         return
 
     import numpy as np
@@ -394,7 +410,8 @@ def main():
         torch.cuda.empty_cache()
         result["prefill_161k"] = prefill_leg(H, torch, synth)
         torch.cuda.empty_cache()
-        result["single_layer_8seqs_ctx32k"] = single_layer_leg(H, torch, synth)
+        result["single_layer_8seqs_ctx32k"] = single_layer_leg(H, torch, synth,
+                                                               split_tokens=SINGLE_LAYER_SPLIT)
     if not args.no_cb:
         torch.cuda.empty_cache()
         result["continuous_batch_32seq"] = cb_leg(args, H, torch, synth)
