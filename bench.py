@@ -748,7 +748,8 @@ def single_layer_leg(H, torch, synth, steps=50, split_tokens=0):
     the printed policy's layer 0 (4096 x2, 16384 x2, 65536 x4), context
     32,768 per sequence (so the 64K heads read all 32,768 tokens).  A step
     appends each sequence's new token and attends (appending split + merge,
-    two launches); contexts advance by one per step."""
+    two launches); contexts advance by one per step; 10 untimed steps, then
+    `steps` timed ones."""
     import numpy as np
     dev = torch.device("cuda", 0)
     n_seqs, n_kv, G, d, L0 = 8, 8, 3, 128, 32768
@@ -763,24 +764,26 @@ def single_layer_leg(H, torch, synth, steps=50, split_tokens=0):
                       seq_slots=torch.tensor([b], dtype=torch.int32, device=dev))
         del kh, vh
     q = synth.randn((1, n_seqs, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
-    kn = synth.randn((steps + 5, 1, n_seqs, n_kv, d), torch.bfloat16, g)
-    vn = synth.randn((steps + 5, 1, n_seqs, n_kv, d), torch.bfloat16, g)
-    pos = [torch.full((n_seqs,), L0 + i, dtype=torch.int64, device=dev) for i in range(steps + 5)]
+    n_warm = 10
+    kn = synth.randn((steps + n_warm, 1, n_seqs, n_kv, d), torch.bfloat16, g)
+    vn = synth.randn((steps + n_warm, 1, n_seqs, n_kv, d), torch.bfloat16, g)
+    pos = [torch.full((n_seqs,), L0 + i, dtype=torch.int64, device=dev)
+           for i in range(steps + n_warm)]
     ws = H.make_workspace(lay, 0, 1, n_seqs, n_kv * G, device=dev)
     out = torch.empty((1, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
     scale = 1.0 / math.sqrt(d)
     s = torch.cuda.current_stream()
-    for i in range(5):
+    for i in range(n_warm):
         H.hwkv_decode_append_attn(cache, 0, 1, pos[i], kn[i], vn[i], q, scale, ws, out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    for i in range(5, steps + 5):
+    for i in range(n_warm, steps + n_warm):
         H.hwkv_decode_append_attn(cache, 0, 1, pos[i], kn[i], vn[i], q, scale, ws, out)
     e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    tok_heads = float(np.minimum(w.astype(np.int64), L0 + 5 + steps // 2).sum()) * n_seqs
+    tok_heads = float(np.minimum(w.astype(np.int64), L0 + n_warm + steps // 2).sum()) * n_seqs
     b = tok_heads * KV_BYTES_PER_TOK_HEAD
     return {"workload": "1 layer, 8 seqs at context 32768, windows 4096x2/16384x2/65536x4, "
                         "8x3 heads, d=128, bf16",
