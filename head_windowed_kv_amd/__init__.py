@@ -536,11 +536,12 @@ def make_prefill_workspace(layout: Layout, layer: int, n_seqs: int, n_chunk: int
 
 
 def hwkv_prefill_attn(cache: Cache, layer: int, pos0: torch.Tensor, q: torch.Tensor,
-                      k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+                      k: torch.Tensor, v: torch.Tensor, workspace: Optional[torch.Tensor],
                       out: torch.Tensor, scale: float, seq_slots: Optional[torch.Tensor] = None,
                       stream=None) -> None:
     """q, out: [n_seqs][n_chunk][n_q_heads][head_dim]; k, v: [n_seqs][n_chunk][n_kv][head_dim].
-    P enters the P.V product in fp16; workspace: make_prefill_workspace."""
+    P enters the P.V product in fp16; workspace: make_prefill_workspace (None
+    for fp16 caches, which need none)."""
     _prefill(_lib.hwkv_prefill_attn, cache, layer, pos0, q, k, v, workspace, out, scale,
              seq_slots, stream)
 
@@ -569,10 +570,14 @@ def _prefill(fn, cache, layer, pos0, q, k, v, workspace, out, scale, seq_slots, 
             _ptr(pos0), int(q.shape[1]), int(q.shape[2]), _ptr(q), _ptr(k), _ptr(v))
     tail = (_ptr(out), _dtype_code(out.dtype), scale, _stream(stream))
     if fn is _lib.hwkv_prefill_attn:
-        if workspace is None or workspace.dtype != torch.uint8 or workspace.device != out.device:
+        # None is passed on as a null workspace of 0 bytes, which the library
+        # accepts only where none is needed (fp16 caches)
+        if workspace is not None and (workspace.dtype != torch.uint8 or
+                                      workspace.device != out.device):
             raise ValueError("workspace must be a uint8 tensor on the device of out "
                              "(make_prefill_workspace)")
-        _check(fn(*head, _ptr(workspace), workspace.numel(), *tail))
+        _check(fn(*head, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                  *tail))
     else:
         _check(fn(*head, *tail))
 

@@ -161,6 +161,40 @@ def test_f16_output_default_entry():
     _check(to_host_f64(c16.run(out_dtype=torch.float16)), c16.oracle())
 
 
+def test_workspace_rules():
+    """fp16 caches need no workspace (a null one is accepted and the result is
+    that of a call with one); bf16 caches refuse a null or short workspace
+    before launching anything, and a larger one changes nothing."""
+    H = hw()
+    dev = device()
+    say("prefill workspace rules")
+    c16 = PrefillCase([64, 130, 2000], 128, 2, [500, 0], 100, seed=411, dtype=torch.float16)
+    assert H.hwkv_prefill_workspace_bytes(c16.lay, 0, 2, 100) == 0
+    with_ws = c16.run()
+    pos = torch.tensor(c16.pos0, device=dev)
+    out = torch.full_like(with_ws, float("nan"))
+    H.hwkv_prefill_attn(c16.cache, 0, pos, c16.q, c16.k, c16.v, None, out, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(out, with_ws)
+    c = PrefillCase([64, 700], 128, 3, [500, 40], 33, seed=412)
+    good = c.run()
+    need = H.hwkv_prefill_workspace_bytes(c.lay, 0, 2, 33)
+    assert need == 2 * ((63 + 33) + (699 + 33)) * 256
+    pos = torch.tensor(c.pos0, device=dev)
+    out = torch.zeros_like(good)
+    for ws, status in ((None, "HWKV_ERR_INVALID_ARG"), (c.ws[:need - 256], "HWKV_ERR_CAPACITY")):
+        with pytest.raises(H.HwkvError) as e:
+            H.hwkv_prefill_attn(c.cache, 0, pos, c.q, c.k, c.v, ws, out, 1 / math.sqrt(128))
+        assert e.value.status_name == status
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)  # nothing was launched
+    big = H._alloc_aligned(need + (1 << 20), dev)
+    big.fill_(0x7F)
+    H.hwkv_prefill_attn(c.cache, 0, pos, c.q, c.k, c.v, big, out, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(out, good)
+
+
 def test_chunk_size_invariance_and_last_row_equals_decode():
     """Prefill n rows at once == prefill n1, append n1, prefill the rest; the
     last row equals a decode step at L = P + n after appending the chunk.
