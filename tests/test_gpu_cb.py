@@ -3,9 +3,12 @@
 32 sequences with contexts uniform in [4K, 160K] plus one sequence per
 window level starting 100 tokens before its window edge (so that 256 steps
 cross the edge and wrap the ring), 48 layers with the stack's windows, 256
-decode steps of append + attention, each step one append, one split and one
-merge launch for all layers and sequences (the launch pattern of the
-continuous-batch benchmark).
+decode steps of append + attention, each step one appending split launch
+(which also writes every sequence's new token) and one merge launch for all
+layers and sequences: the launch pattern of the continuous-batch benchmark.
+The benchmark writes bf16 outputs; at each checkpoint a non-appending
+decode of the same state with bf16 output must equal the step's fp32 output
+rounded to bf16, bit for bit.
 
 The pool starts filled with N(0,1) bf16 values (synthetic input); by the
 ring placement every slot of a head's ring then holds the token of one of
@@ -81,6 +84,7 @@ def test_continuous_batch_sampled():
     L0_t = torch.tensor(L0, dtype=torch.int64, device=dev)
     ws = H.make_workspace(lay, 0, n_layers, n_seqs, n_kv * G, device=dev)
     out = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.float32, device=dev)
+    out16 = torch.empty((n_layers, n_seqs, n_kv * G, d), dtype=torch.bfloat16, device=dev)
     g = synth.gen(108, dev)
     sb = torch.tensor([s[0] for s in samples], device=dev)
     sl = torch.tensor([s[1] for s in samples], device=dev)
@@ -92,14 +96,16 @@ def test_continuous_batch_sampled():
         vn = synth.randn((n_layers, n_seqs, 1, n_kv, d), torch.bfloat16, g)
         q = synth.randn((n_layers, n_seqs, n_kv * G, d), torch.bfloat16, g,
                         std=1.0 / math.sqrt(d))
-        H.hwkv_append(cache, 0, n_layers, L0_t + i, kn, vn)
-        H.hwkv_decode_attn(cache, 0, n_layers, L0_t + i + 1, q, 1.0 / math.sqrt(d), ws, out)
+        H.hwkv_decode_append_attn(cache, 0, n_layers, L0_t + i, kn, vn, q, 1.0 / math.sqrt(d),
+                                  ws, out)
         k_rec.append(kn[sl, sb, 0, shh].clone())
         v_rec.append(vn[sl, sb, 0, shh].clone())
         qg = q.view(n_layers, n_seqs, n_kv, G, d)
         q_rec.append(qg[sl, sb, shh].clone())
         if i in CHECKPOINTS:
             o_rec[i] = out.view(n_layers, n_seqs, n_kv, G, d)[sl, sb, shh].clone()
+            H.hwkv_decode_attn(cache, 0, n_layers, L0_t + i + 1, q, 1.0 / math.sqrt(d), ws, out16)
+            assert torch.equal(out16, out.to(torch.bfloat16)), i
     torch.cuda.synchronize()
     say("cb: oracle on", len(samples), "heads x", len(CHECKPOINTS), "checkpoints")
     k_rec = synth.to_raw(torch.stack(k_rec))  # [steps][samples][d]

@@ -249,7 +249,14 @@ def test_prefill_config_161k_then_append_and_decode():
     say("prefill 161K config: fill")
     c = PrefillCase(list(synth.YAML_LAYER0), d, G, [P] * 4, n, seed=105)
     say("prefill 161K config: run")
-    got = to_host_f64(c.run())
+    out32 = c.run()
+    got = to_host_f64(out32)
+    # the benchmark's launch writes bf16: the same fp32 results rounded to
+    # nearest even, bit for bit
+    say("prefill 161K config: bf16 output")
+    out16 = c.run(out_dtype=torch.bfloat16)
+    assert torch.equal(out16, out32.to(torch.bfloat16))
+    del out16, out32
     rng = np.random.default_rng(7)
     rows = sorted(set([0, 1, 31, 32, 63, 64, 1023, 1024, 2046, 2047] +
                       list(rng.integers(0, 2048, 14))))
