@@ -238,8 +238,9 @@ def test_stack48_step_full_size():
     """The 48-layer 112K stack (windows from {1K,4K,16K,64K}, seed 0, batch 1):
     the single-launch step and the two-launch step (the split stage appends;
     the benchmark's headline launches) equal the append + split + merge
-    launches bit for bit over every output row and the whole pool, and
-    sampled layers match the oracle."""
+    launches bit for bit over every output row and the whole pool, the bf16
+    output the benchmark writes is those results rounded to bf16, and sampled
+    layers match the oracle."""
     H = hw()
     dev = device()
     w = synth.stack_windows(48, 8, 0)
@@ -266,6 +267,12 @@ def test_stack48_step_full_size():
     torch.cuda.synchronize()
     assert torch.equal(o_e, o_t)
     assert torch.equal(t.cache.pool, f.cache.pool)
+    # the headline writes bf16: the same results rounded to nearest even
+    say("stack48 two launches: bf16 output")
+    o16 = torch.empty(o_t.shape, dtype=torch.bfloat16, device=dev)
+    H.hwkv_decode_attn(t.cache, 0, 48, pos + 1, t.q, 1.0 / math.sqrt(128), ws2, o16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o_t.to(torch.bfloat16))
     del t
     got = to_host_f64(o_f)
     worst = 0.0
