@@ -205,6 +205,16 @@ def test_single_layer_config(split):
     say("single-layer max row rel err", err)
     assert err <= BF16_TOL
     assert err <= DECODE_REGRESSION_TOL, err
+    # the benchmark's launch: the appending split (rewriting the same token)
+    # and the merge, bf16 output = the fp32 results rounded to bf16
+    H = hw()
+    dev = device()
+    ws = H.make_workspace(c.lay, 0, 1, 8, 24, device=dev)
+    o16 = torch.empty((1, 8, 24, 128), dtype=torch.bfloat16, device=dev)
+    H.hwkv_decode_append_attn(c.cache, 0, 1, torch.full((8,), 32768, device=dev), c.k_new,
+                              c.v_new, c.q, 1.0 / math.sqrt(128), ws, o16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, out.to(torch.bfloat16))
 
 
 def test_stack48_config():
