@@ -758,6 +758,7 @@ template <int D>
 hwkv_status launch_v16(const PrefillArgs& a, hipStream_t s) {
     // about 2048 workgroups over the whole grid, at most 256 per pair
     const int64_t pairs = (int64_t)a.n_seqs * a.n_kv_heads;
+    if (pairs > 0x7fffffff) return fail(HWKV_ERR_OVERFLOW, "prefill pre-pass grid too large");
     const int64_t per = (2048 + pairs - 1) / pairs;
     dim3 grid((unsigned)pairs, (unsigned)(per < 256 ? per : 256));
     hipLaunchKernelGGL(prefill_v16_kernel<D>, grid, dim3(256), 0, s, a);
