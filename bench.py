@@ -49,6 +49,11 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the 161K chunked-prefill leg (e.g. under rocprofv3 --pmc)")
+    p.add_argument("--no-mixed", action="store_true",
+                   help="skip the mixed-stack leg (fp16 / 64-token blocks, hybrid SWA + "
+                        "global stack, head_dim 256 prefill)")
+    p.add_argument("--mixed-only", action="store_true",
+                   help="run only the mixed-stack leg (e.g. under rocprofv3)")
     p.add_argument("--single-layer-only", action="store_true",
                    help="run only the one-layer, 8-sequence, 32K-context decode leg (e.g. "
                         "under rocprofv3)")
@@ -224,6 +229,14 @@ def main():
         import synth
         torch.cuda.set_device(0)
         print(json.dumps({"prefill_161k": prefill_leg(H, torch, synth)}), flush=True)
+        return
+    if args.mixed_only:
+        import torch
+
+        import head_windowed_kv_amd as H
+        import synth
+        torch.cuda.set_device(0)
+        print(json.dumps({"mixed_stacks": mixed_leg(H, torch, synth)}), flush=True)
         return
     if args.single_layer_only:
         import torch
@@ -412,6 +425,9 @@ def main():
         torch.cuda.empty_cache()
         result["single_layer_8seqs_ctx32k"] = single_layer_leg(H, torch, synth,
                                                                split_tokens=SINGLE_LAYER_SPLIT)
+        torch.cuda.empty_cache()
+        if not args.no_mixed:
+            result["mixed_stacks"] = mixed_leg(H, torch, synth)
     if not args.no_cb:
         torch.cuda.empty_cache()
         result["continuous_batch_32seq"] = cb_leg(args, H, torch, synth)
@@ -741,6 +757,130 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
             "launches_per_step": {"single_launch": 1, "append_in_split": 2}.get(mode, 3) * n_layers,
             "replays": n_rep,
             "split_tokens": lay.desc().split_tokens}
+
+
+def stack_decode_time(H, torch, synth, windows, dtype, block_size, L0, steps=20, n_warm=10,
+                      seed=0):
+    """One decode step per call over a whole stack (batch 1): the appending
+    split + merge for all layers (hwkv_decode_append_attn, bf16 outputs),
+    after filling each layer with the last min(L0, capacity) positions of
+    N(0,1) history; `n_warm` untimed steps, then `steps` timed as one block."""
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    windows = np.asarray(windows, np.int32)
+    n_layers, n_kv = windows.shape
+    G, d = 3, 128
+    lay = H.hwkv_layout_create(windows, block_size, d, dtype)
+    cache = H.make_cache(lay, 1, device=dev)
+    cap = int(((windows.astype(np.int64) + block_size - 1) // block_size * block_size).max())
+    n_hist = min(L0, cap)
+    pos_hist = torch.full((1,), L0 - n_hist, dtype=torch.int64, device=dev)
+    for l in range(n_layers):
+        g = synth.gen(seed * 100003 + l, dev)
+        k = synth.randn((1, 1, n_hist, n_kv, d), dtype, g)
+        v = synth.randn((1, 1, n_hist, n_kv, d), dtype, g)
+        H.hwkv_append(cache, l, 1, pos_hist, k, v)
+        del k, v
+    g = synth.gen(seed + 1, dev)
+    n = steps + n_warm
+    q = synth.randn((n_layers, 1, n_kv * G, d), dtype, g, std=1.0 / math.sqrt(d))
+    kn = synth.randn((n, n_layers, 1, 1, n_kv, d), dtype, g)
+    vn = synth.randn((n, n_layers, 1, 1, n_kv, d), dtype, g)
+    pos = [torch.full((1,), L0 + i, dtype=torch.int64, device=dev) for i in range(n)]
+    ws = H.make_workspace(lay, 0, n_layers, 1, n_kv * G, device=dev)
+    out = torch.empty((n_layers, 1, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    for i in range(n_warm):
+        H.hwkv_decode_append_attn(cache, 0, n_layers, pos[i], kn[i], vn[i], q, scale, ws, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_warm, n):
+        H.hwkv_decode_append_attn(cache, 0, n_layers, pos[i], kn[i], vn[i], q, scale, ws, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    b = float(np.minimum(windows.astype(np.int64), L0 + n_warm + steps // 2).sum()) * \
+        KV_BYTES_PER_TOK_HEAD
+    del cache, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(1.0 / (ms / 1e3), 1),
+            "kv_read_bytes_per_step": b, "kv_read_gbps": round(b / (ms / 1e3) / 1e9, 1),
+            "kv_read_frac_of_peak": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "steps": steps, "split_tokens": lay.desc().split_tokens}
+
+
+def prefill_time(H, torch, synth, d, reps=10):
+    """hwkv_prefill_attn alone on the 161K chunk of prefill_leg (4 sequences,
+    8 KV x 3 heads, bf16, printed layer-0 windows, 2048-token chunk at
+    P = 164,864) at head dimension d."""
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    n_seqs, n_kv, G, n = 4, 8, 3, 2048
+    P = synth.CTX_161K
+    w = np.array([synth.YAML_LAYER0], np.int32)
+    lay = H.hwkv_layout_create(w, 16, d, torch.bfloat16)
+    cache = H.make_cache(lay, n_seqs, device=dev)
+    cap = int(((w.astype(np.int64) + 15) // 16 * 16).max())
+    for b in range(n_seqs):
+        g = synth.gen(105 * 100003 + b, dev)
+        kh = synth.randn((1, 1, cap, n_kv, d), torch.bfloat16, g)
+        vh = synth.randn((1, 1, cap, n_kv, d), torch.bfloat16, g)
+        H.hwkv_append(cache, 0, 1, torch.tensor([P - cap], device=dev), kh, vh,
+                      seq_slots=torch.tensor([b], dtype=torch.int32, device=dev))
+        del kh, vh
+    g = synth.gen(106, dev)
+    q = synth.randn((n_seqs, n, n_kv * G, d), torch.bfloat16, g, std=1.0 / math.sqrt(d))
+    k = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+    v = synth.randn((n_seqs, n, n_kv, d), torch.bfloat16, g)
+    out = torch.empty((n_seqs, n, n_kv * G, d), dtype=torch.bfloat16, device=dev)
+    pos = torch.full((n_seqs,), P, dtype=torch.int64, device=dev)
+    pws = H.make_prefill_workspace(lay, 0, n_seqs, n, device=dev)
+    for _ in range(2):
+        H.hwkv_prefill_attn(cache, 0, pos, q, k, v, pws, out, 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        H.hwkv_prefill_attn(cache, 0, pos, q, k, v, pws, out, 1.0 / math.sqrt(d))
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[len(ts) // 2]
+    keys = sum(min(int(wh), P + r + 1) for wh in w[0] for r in range(n))
+    flop = 4.0 * d * G * keys * n_seqs
+    del cache, pws
+    torch.cuda.empty_cache()
+    return {"head_dim": d, "prefill_ms": round(ms, 4), "prefill_flop": flop,
+            "prefill_tflops": round(flop / (ms / 1e3) / 1e12, 1),
+            "mfma_frac_of_bf16_peak": round(flop / (ms / 1e3) / 2.5e15, 4)}
+
+
+def mixed_leg(H, torch, synth):
+    """Mixed stacks through the same entry points (the 48-layer stacks at
+    context 112K, batch 1, one appending split + merge per step for all
+    layers): the headline's windows on an fp16 cache in 64-token blocks, and
+    a hybrid stack of sliding-window layers (every head 4096 tokens) with
+    every fourth layer a per-head global layer; then the 161K chunked prefill
+    at head_dim 256."""
+    L0 = synth.CTX_112K
+    res = {"stack48_f16_block64": stack_decode_time(
+               H, torch, synth, synth.stack_windows(48, 8, 0), torch.float16, 64, L0, seed=111),
+           "hybrid48_swa4096_every4th_global": stack_decode_time(
+               H, torch, synth, synth.hybrid_windows(48, 8, 4096, 4, 0), torch.bfloat16, 16, L0,
+               seed=112),
+           "prefill_161k_head_dim256": prefill_time(H, torch, synth, 256)}
+    res["stack48_f16_block64"]["workload"] = (
+        "48 layers x 8x3 heads, d=128, fp16, block size 64, windows of the headline (seed 0), "
+        "context 112K, batch 1")
+    res["hybrid48_swa4096_every4th_global"]["workload"] = (
+        "48 layers x 8x3 heads, d=128, bf16, bs 16: layers 3, 7, ..., 47 per-head windows of the "
+        "headline draw, all others every head 4096 (sliding window), context 112K, batch 1")
+    res["prefill_161k_head_dim256"]["workload"] = (
+        "the 161K chunk of prefill_161k (4 seqs, 2048 rows at P=164864, layer-0 windows, 8x3 "
+        "heads, bf16) at head_dim 256")
+    return res
 
 
 def single_layer_leg(H, torch, synth, steps=50, split_tokens=0):

@@ -38,6 +38,16 @@ def stack_windows(n_layers: int = 48, n_kv_heads: int = 8, seed: int = 0) -> np.
     return w.astype(np.int32)
 
 
+def hybrid_windows(n_layers: int = 48, n_kv_heads: int = 8, swa: int = 4096, every: int = 4,
+                   seed: int = 0) -> np.ndarray:
+    """A hybrid stack: layer l with l % every == every - 1 is a global layer
+    whose per-head windows are those of ``stack_windows(..., seed)``; every
+    other layer is a sliding-window layer whose heads all keep ``swa`` tokens."""
+    w = stack_windows(n_layers, n_kv_heads, seed)
+    w[(np.arange(n_layers) % every) != every - 1] = swa
+    return w
+
+
 def gen(seed: int, device="cpu") -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))

@@ -222,14 +222,15 @@ class StackCase:
     v_new: torch.Tensor
 
 
-def build_stack_case(windows, dtype, head_dim, group, L, n_seqs, seed, split_tokens=0):
+def build_stack_case(windows, dtype, head_dim, group, L, n_seqs, seed, split_tokens=0,
+                     block_size=16):
     H = hw()
     dev = device()
     windows = np.asarray(windows, np.int32)
     n_layers, n_kv = windows.shape
-    lay = H.hwkv_layout_create(windows, 16, head_dim, dtype, split_tokens)
+    lay = H.hwkv_layout_create(windows, block_size, head_dim, dtype, split_tokens)
     cache = H.make_cache(lay, n_seqs, device=dev, fill=0xFF)
-    cap = int(((windows.astype(np.int64) + 15) // 16 * 16).max())
+    cap = int(((windows.astype(np.int64) + block_size - 1) // block_size * block_size).max())
     n_hist = min(L, cap)
     base = L - n_hist
     q = synth.randn((n_layers, n_seqs, n_kv * group, head_dim), dtype, synth.gen(seed, dev),

@@ -14,8 +14,9 @@ import pytest
 import torch
 
 import synth
-from _gpu_common import (build_decode_case, device, hw, oracle_decode, row_rel_err,
-                         run_decode_step, say, to_host_f64, tol)
+from _gpu_common import (build_decode_case, build_stack_case, device, hw, oracle_decode,
+                         row_rel_err, run_decode_step, say, stack_oracle_layer, stack_step,
+                         to_host_f64, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,3 +143,37 @@ def test_full_attention_layer_equals_all_tokens():
                           hist_margin=10 ** 7)
     assert c.base == [0, 0]
     _check(c, run_decode_step(c))
+
+
+@pytest.mark.parametrize("kind", ["stack48_f16_block64", "hybrid48_swa4096_every4th_global"])
+def test_mixed_stack_configs_at_full_size(kind):
+    """The mixed-stack configurations the benchmark times, at full size (48
+    layers, context 112K, batch 1): the headline's windows on an fp16 cache in
+    64-token blocks, and the hybrid stack (sliding-window layers of 4096 with
+    every fourth layer per-head global).  Sampled sliding-window and global
+    layers against the oracle; the benchmark's launch (appending split + merge
+    with bf16 output) equals the three-launch step's fp32 results rounded."""
+    H = hw()
+    dev = device()
+    if kind == "stack48_f16_block64":
+        windows, dtype, bs, layers = synth.stack_windows(48, 8, 0), torch.float16, 64, (0, 23, 47)
+    else:
+        windows, dtype, bs, layers = synth.hybrid_windows(48, 8, 4096, 4, 0), torch.bfloat16, 16, \
+            (0, 3, 22, 47)
+    say("mixed config", kind, ": fill")
+    c = build_stack_case(windows, dtype, 128, 3, synth.CTX_112K, 1, seed=706, block_size=bs)
+    say("mixed config", kind, ": step")
+    out = stack_step(c)
+    got = to_host_f64(out)
+    assert np.all(np.isfinite(got))
+    worst = 0.0
+    for l in layers:
+        worst = max(worst, row_rel_err(got[l:l + 1], stack_oracle_layer(c, l)))
+    say("mixed config", kind, "max row rel err (sampled layers)", worst)
+    assert worst <= tol(dtype)
+    ws = H.make_workspace(c.lay, 0, 48, 1, 24, device=dev)
+    o16 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
+    H.hwkv_decode_append_attn(c.cache, 0, 48, torch.tensor([synth.CTX_112K], device=dev),
+                              c.k_new, c.v_new, c.q, 1.0 / math.sqrt(128), ws, o16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, out.to(torch.bfloat16))
