@@ -431,7 +431,7 @@ hwkv_status hwkv_prefill_attn(const hwkv_layout *layout, const hwkv_cache *cache
 /* hwkv_prefill_attn with the P.V product at ~16-bit precision for BF16
  * caches: P is split into its truncation to bf16 and the remainder rounded
  * to bf16, two bf16 products (row error ~1e-5 of the row's largest output),
- * at about 10% more time; one kernel, no workspace.  For F16 caches it is
+ * at about 25-30% more time; one kernel, no workspace.  For F16 caches it is
  * hwkv_prefill_attn.  Same arguments (without the workspace), layouts and
  * errors. */
 hwkv_status hwkv_prefill_attn_exact(const hwkv_layout *layout,
