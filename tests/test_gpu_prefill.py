@@ -195,6 +195,17 @@ def test_workspace_rules():
     assert torch.equal(out, good)
 
 
+def test_many_sequences():
+    """260 sequences x 8 KV heads (2080 (sequence, kv head) pairs: the V
+    pre-pass gives each pair one workgroup), ragged positions, every row of
+    every sequence against the oracle."""
+    say("prefill many sequences")
+    rng = np.random.default_rng(9)
+    pos0 = [int(x) for x in rng.integers(0, 700, 260)]
+    c = PrefillCase([16, 64, 100, 300, 33, 1, 257, 200], 128, 3, pos0, 40, seed=413)
+    _check(to_host_f64(c.run()), c.oracle())
+
+
 def test_chunk_size_invariance_and_last_row_equals_decode():
     """Prefill n rows at once == prefill n1, append n1, prefill the rest; the
     last row equals a decode step at L = P + n after appending the chunk.
