@@ -440,6 +440,19 @@ def test_decode_argument_errors_before_launch():
     # non-finite scale
     assert f(lay.handle, ctypes.byref(cv), 0, 1, 1, None, ctx, 4, q, float("inf"), ws, need, out,
              0, None) == 1
+    # batch sizes outside [1, 65535] (the sequences are a grid dimension)
+    slots = ctypes.c_void_p(12 << 20)
+    for n_seqs in (0, -1, 65536):
+        assert f(lay.handle, ctypes.byref(cv), 0, 1, n_seqs, slots, ctx, 4, q, 0.1, ws, 1 << 40,
+                 out, 0, None) == 1, n_seqs
+        assert "n_seqs" in hw.hwkv_last_error()
+    lay_p = hw.hwkv_layout_create([[32, 128]], 16, 128, "bf16")
+    cvp = _fake_cache(lay_p, hw.hwkv_mem_estimate(lay_p, 1), 1)
+    for n_seqs in (0, 65536):
+        assert hw._lib.hwkv_prefill_attn(lay_p.handle, ctypes.byref(cvp), 0, n_seqs, slots, ctx,
+                                         7, 4, q, ctypes.c_void_p(5 << 20),
+                                         ctypes.c_void_p(6 << 20), ws, 1 << 40, out, 0, 0.1,
+                                         None) == 1, n_seqs
 
 
 def test_static_scratch_entry_refuses_calls_beyond_its_array():
