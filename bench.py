@@ -70,7 +70,8 @@ def parse():
                         "copy of known size (the counters' calibration)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
-                        "into profiles/decode_split_stack48_counters.json and exit")
+                        "into profiles/decode_split_stack48_counters.json (with --config cb: "
+                        "decode_split_cb_counters.json) and exit")
     return p.parse_args()
 
 
@@ -82,11 +83,18 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(split_tokens: int):
+COUNTER_FILES = {"stack48": "decode_split_stack48_counters.json",
+                 "cb": "decode_split_cb_counters.json"}
+COUNTER_COMMANDS = {
+    "stack48": "python -u bench.py --counter-pass --steps 3 --warmup 2",
+    "cb": "python -u bench.py --config cb --counter-pass --cb-steps 4"}
+
+
+def load_traffic(split_tokens: int, workload: str = "stack48"):
     """HBM traffic of one split launch from committed rocprofv3 counter runs,
     valid only while the kernel source and split size are the ones the
     counters were taken on."""
-    path = os.path.join(ROOT, "profiles", "decode_split_stack48_counters.json")
+    path = os.path.join(ROOT, "profiles", COUNTER_FILES[workload])
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -180,16 +188,18 @@ def _pmc_rows(folder, counter):
     return rows
 
 
-def summarize_counters(fetch_dir, write_dir, split_tokens):
+def summarize_counters(fetch_dir, write_dir, split_tokens, workload="stack48"):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel, each
-    scaled by what the same counter reads for the probe copy of known size."""
+    scaled by what the same counter reads for the probe copy of known size;
+    workload: the 48-layer headline step (stack48) or the continuous batch
+    (cb), whose counter passes each run the probe copy too."""
     import head_windowed_kv_amd as H
     import synth
     lay = H.hwkv_layout_create(synth.stack_windows(48, 8, 0), 16, 128, "bf16", split_tokens)
     out = {"kernel_source_sha": kernel_source_sha(), "probe_copy_bytes": PROBE_COPY_BYTES,
-           "split_tokens": lay.desc().split_tokens,
-           "command": "rocprofv3 --pmc <COUNTER> --output-format csv -d <dir> -o run -- "
-                      "python -u bench.py --counter-pass --steps 3 --warmup 2"}
+           "split_tokens": lay.desc().split_tokens, "workload": workload,
+           "command": "rocprofv3 --pmc <COUNTER> --output-format csv -d <dir> -o run -- " +
+                      COUNTER_COMMANDS[workload]}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(folder, counter)
         split = [v for n, v in rows if "decode_split_kernel" in n]
@@ -204,7 +214,7 @@ def summarize_counters(fetch_dir, write_dir, split_tokens):
                         "dispatches": len(split)}
     out["traffic_bytes_per_launch"] = (out["FETCH_SIZE"]["split_bytes_scaled"] +
                                        out["WRITE_SIZE"]["split_bytes_scaled"])
-    path = os.path.join(ROOT, "profiles", "decode_split_stack48_counters.json")
+    path = os.path.join(ROOT, "profiles", COUNTER_FILES[workload])
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -213,7 +223,7 @@ def summarize_counters(fetch_dir, write_dir, split_tokens):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.split_tokens)
+        summarize_counters(*args.summarize_counters, args.split_tokens, args.config)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -447,6 +457,8 @@ def cb_run(args):
     import synth
     torch.cuda.set_device(0)
     leg = cb_leg(args, H, torch, synth)
+    if args.counter_pass:  # the counters' calibration, as in the headline's counter pass
+        probe_copy_once(torch, torch.device("cuda", 0))
     res = {"metric": METRIC, "value": leg["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
            "steps": leg["steps"], "warmup": 2, "ms_per_step": leg["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -540,7 +552,14 @@ def cb_leg(args, H, torch, synth):
                       "layers and 32 sequences",
             "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16, d128, G3, append>",
                          "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic(lay.desc().split_tokens, "cb"),
+                         "traffic_source": "committed rocprofv3 --pmc counters (FETCH_SIZE, "
+                                           "WRITE_SIZE per dispatch, scaled by the probe copy "
+                                           "of known size) in profiles/"
+                                           "decode_split_cb_counters.json; reported only while "
+                                           "the kernel source hash and split length match "
+                                           "(else null)",
                          "avg_launch_ms": round(split_ms, 4),
                          "algorithmic_bytes_per_launch": roof_bytes / n_roof,
                          "avg_launch_timing": "HIP events around each split launch, %d steps "
