@@ -66,7 +66,7 @@ bool append_supported(const hwkv_layout& lay) {
     return ((int64_t)lay.head_dim * elem_bytes(lay.dtype)) % 16 == 0;
 }
 
-hwkv_status launch_append(const hwkv_layout& lay, const AppendArgs& a, hipStream_t s) {
+hwkv_status launch_append(const hwkv_layout& /*lay*/, const AppendArgs& a, hipStream_t s) {
     int64_t blocks = (a.n_chunks + kThreads - 1) / kThreads;
     if (blocks > 16384) blocks = 16384;
     if (blocks < 1) return HWKV_OK;
