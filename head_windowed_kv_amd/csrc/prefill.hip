@@ -438,14 +438,29 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
     auto qk = [&](const uint8_t* kt, f32x16& s0, f32x16& s1) {
         s0 = f32x16{};
         s1 = f32x16{};
+        u32x4 ka[C::KSTEP][2];
 #pragma unroll
         for (int s = 0; s < C::KSTEP; s++) {
             const uint32_t off = kx ^ (uint32_t)(32 * s);
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + off);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + 32 * C::ROW + off);
-            s0 = mfma32<KT>(a0, qop[s], s0);
-            s1 = mfma32<KT>(a1, qop[s], s1);
+            ka[s][0] = *reinterpret_cast<const u32x4*>(kt + off);
+            ka[s][1] = *reinterpret_cast<const u32x4*>(kt + 32 * C::ROW + off);
         }
+#pragma unroll
+        for (int s = 0; s < C::KSTEP; s++) {
+            s0 = mfma32<KT>(ka[s][0], qop[s], s0);
+            s1 = mfma32<KT>(ka[s][1], qop[s], s1);
+        }
+        // keep the K operand reads three k-steps ahead of the MFMAs that use
+        // them (the compiler alone keeps about one, which leaves LDS latency
+        // exposed): 6 LDS reads, then 2 MFMAs and 2 reads per k-step
+        static_assert(C::KSTEP >= 3, "three k-steps of look-ahead");
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+#pragma unroll
+        for (int s = 0; s < C::KSTEP - 3; s++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     };
 
     // mask keys outside [pq-w+1, pq] (with u = pq - t, keep 0 <= u < w) and
