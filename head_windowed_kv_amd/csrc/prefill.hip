@@ -535,18 +535,20 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
         }
     };
 
-    // O^T += V^T P^T for k-step ks; the V^T operands come from transpose reads
-    // (fp16 when F16P: an fp16 cache, or the pre-pass's fp16 copy of a bf16 cache)
-    auto pv = [&](auto f16p_tag, const uint8_t* vt, int ks, const u32x4& hi, const u32x4& lo) {
-        constexpr bool F16P = decltype(f16p_tag)::value;
+    // V^T operands of k-step ks from transpose reads (fp16 when F16P: an fp16
+    // cache, or the pre-pass's fp16 copy of a bf16 cache)
+    auto vread = [&](const uint8_t* vt, int ks, u32x4* va) {
         const int roff = ((ks >> 1) * 32 + (ks & 1) * 16) * C::ROW;
-        u32x4 va[C::DBLK];
 #pragma unroll
         for (int db = 0; db < C::DBLK; db++) {
             const u32x2 r0 = tr_read(vt + roff + vaddr[db]);
             const u32x2 r1 = tr_read(vt + roff + 8 * C::ROW + vaddr[db]);
             va[db] = u32x4{r0.x, r0.y, r1.x, r1.y};
         }
+    };
+    // O^T += V^T P^T for one k-step
+    auto pv = [&](auto f16p_tag, const u32x4* va, const u32x4& hi, const u32x4& lo) {
+        constexpr bool F16P = decltype(f16p_tag)::value;
         if constexpr (F16P) {
 #pragma unroll
             for (int db = 0; db < C::DBLK; db++) oacc[db] = mfma32<kF16>(va[db], hi, oacc[db]);
@@ -622,14 +624,21 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_kernel(Pref
             u32x4 phi[4], plo[4];
             float psum = 0.f;
             qk(k_rd, s_next[0], s_next[1]);
+            // the V^T operands of each k-step are read one k-step before
+            // its P.V MFMAs (two register sets in turn)
+            u32x4 vA[C::DBLK], vB[C::DBLK];
+            vread(v_rd, 0, vA);
             make_p(f16p_tag, s_cur, 0, phi[0], plo[0], psum);
+            vread(v_rd, 1, vB);
             make_p(f16p_tag, s_cur, 1, phi[1], plo[1], psum);
-            pv(f16p_tag, v_rd, 0, phi[0], plo[0]);
-            pv(f16p_tag, v_rd, 1, phi[1], plo[1]);
+            pv(f16p_tag, vA, phi[0], plo[0]);
+            vread(v_rd, 2, vA);
+            pv(f16p_tag, vB, phi[1], plo[1]);
+            vread(v_rd, 3, vB);
             make_p(f16p_tag, s_cur, 2, phi[2], plo[2], psum);
+            pv(f16p_tag, vA, phi[2], plo[2]);
             make_p(f16p_tag, s_cur, 3, phi[3], plo[3], psum);
-            pv(f16p_tag, v_rd, 2, phi[2], plo[2]);
-            pv(f16p_tag, v_rd, 3, phi[3], plo[3]);
+            pv(f16p_tag, vB, phi[3], plo[3]);
             l_run += psum;
             if (it + 1 < n_tiles) mt = mask_max(s_next, T + 1);
         };
