@@ -45,7 +45,9 @@
 // swizzled against bank conflicts); every wave runs the workgroup's key range
 // (the union of its units' windows, at most a tile or two wider than its
 // own) and masks only the tiles that cross its window start or its causal
-// diagonal.
+// diagonal.  Inside a tile the K operands of S^T are read from LDS three
+// k-steps ahead of their MFMAs and the V^T operands one k-step ahead, so the
+// LDS latency overlaps the matrix work of the same wave.
 #include <hip/hip_runtime.h>
 
 #include "hwkv_internal.h"
