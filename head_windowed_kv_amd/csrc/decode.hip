@@ -156,6 +156,52 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// ---- helpers of the MFMA block loop ----
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16x16x32 MFMA on 16-bit operands of element kind T, fp32 accumulation.
+// Lane l holds A[l % 16][8 (l / 16) .. + 7], B[8 (l / 16) .. + 7][l % 16] and
+// D[4 (l / 16) .. + 3][l % 16].
+template <int T>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (T == kF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Lane j of a 16-lane group reads four consecutive 16-bit elements at `addr`
+// (row j / 4, columns 4 (j % 4) .. + 3 of a 4 x 16 block); the transposing
+// read hands lane i the four rows' elements of column i.
+__device__ __forceinline__ u32x2 tr_read(const uint8_t* addr) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr));
+}
+
+// two fp32 -> packed pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, f16x2_t));
+}
+// two fp32 -> packed bf16 pair, truncated (the high halves of the words)
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// LDS accesses of one wave to its own staging tiles: the hardware performs a
+// wave's LDS instructions in order, so only the compiler must keep them so
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Element type traits: a 16-byte chunk holds EPC elements.
 template <int T>
 struct Elem {
@@ -176,6 +222,24 @@ struct SplitCfg {
     static constexpr int NG = 64 / LPG;          // row groups per wave
     static constexpr int ROWS = kBS / NG;        // rows per group per tile
     static_assert(NC >= 1 && ROW % (16 * LPG) == 0, "rows of whole lane chunks");
+};
+
+// GQA groups of at least this many query heads take the MFMA block loop
+// (16-bit caches).  In the per-lane form the VALU work per byte grows with G
+// (a dot product and a multiply-add per element and query head) and bounds
+// the kernel from G = 4 on; the matrix cores handle a 16-column S^T tile
+// whatever G <= 16 is.
+constexpr int kMfmaMinGroup = 4;
+
+// Geometry of the MFMA block loop for head_dim D (16-bit elements).
+template <int D>
+struct MfmaCfg {
+    static constexpr int KSTEP = D / 32;      // 16x16x32 k-steps of S^T = K Q^T
+    static constexpr int DT = D / 16;         // 16-row tiles of O^T
+    static constexpr int CPR = D / 8;         // 16-byte chunks per K or V row
+    static constexpr int TILE = kBS * D * 2;  // bytes of one tile's K (or V) rows
+    // chunk c of row t sits at chunk c ^ swz(t) of its LDS row
+    static __device__ __forceinline__ int swz(int t) { return t & (CPR < 16 ? CPR - 1 : 15); }
 };
 
 // partial dot product of one row chunk with one query chunk (16-bit
@@ -366,6 +430,14 @@ struct MergeCfg {
     static_assert(NE4 % DS == 0, "merge geometry");
 };
 
+// LDS of one merge: the SG groups' partial numerators, denominators and maxima
+template <int D, int G>
+struct MergeLds {
+    f32x4 num[MergeCfg<D, G>::SG][MergeCfg<D, G>::NE4];
+    float den[MergeCfg<D, G>::SG][G];
+    float mk[MergeCfg<D, G>::SG][G];
+};
+
 // factor that takes a partial kept at running maximum `from` to maximum `to`
 __device__ __forceinline__ float rescale(float from, float to) {
     return from == to ? 1.f : fast_exp2(from - to);
@@ -420,12 +492,12 @@ __device__ __forceinline__ float merge_den_part(const float* rec0, int rec_float
 // NTHREADS threads of a workgroup.  obase: output offset of the head's first
 // element.
 template <int D, int G, int NTHREADS>
-__device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0, int ds1, void* out,
-                             int out_kind, int64_t obase) {
+__device__ void merge_chunks(MergeLds<D, G>& sm, const float* rec0, int ns, int rec_floats, int ds0,
+                             int ds1, void* out, int out_kind, int64_t obase) {
     typedef MergeCfg<D, G> M;
-    __shared__ f32x4 s_num[M::SG][M::NE4];
-    __shared__ float s_den[M::SG][G];
-    __shared__ float s_mk[M::SG][G];
+    auto& s_num = sm.num;
+    auto& s_den = sm.den;
+    auto& s_mk = sm.mk;
     const int t = threadIdx.x;
     const int c0 = ds0 * M::CPS, ncols = (ds1 - ds0) * M::CPS;
     const int npairs = ncols * M::SG + G * M::SG;
@@ -467,9 +539,9 @@ __device__ void merge_chunks(const float* rec0, int ns, int rec_floats, int ds0,
 // split workgroup that finished last: the same operations in the same order
 // as decode_merge_kernel.
 template <int D, int G>
-__device__ void merge_in_workgroup(const float* rec0, int ns, int rec_floats, void* out, int out_kind,
-                                   int64_t obase) {
-    merge_chunks<D, G, kThreads>(rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, out_kind,
+__device__ void merge_in_workgroup(MergeLds<D, G>& sm, const float* rec0, int ns, int rec_floats,
+                                   void* out, int out_kind, int64_t obase) {
+    merge_chunks<D, G, kThreads>(sm, rec0, ns, rec_floats, 0, MergeCfg<D, G>::DS, out, out_kind,
                                  obase);
 }
 
@@ -484,9 +556,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     typedef typename Elem<T>::Chunk Chunk;
     constexpr bool FUSED = MODE == kModeFused;     // merges in the last split
     constexpr bool APPENDS = MODE != kModePlain;  // ctx_len holds positions; appends
+    constexpr bool MF = T != kF32 && G >= kMfmaMinGroup;  // MFMA block loop
+    static_assert(!MF || G <= 16, "one 16-column S^T tile per GQA group");
+    // Partial states the workgroup merge adds up: one per half wave in the
+    // per-lane form, one per wave in the MFMA form.  The MFMA form stages the
+    // K and V rows of two tiles per wave in LDS; the merge reuses that memory
+    // once every wave has left its loop.
+    constexpr int SLOTS = MF ? kWaves : 2 * kWaves;
+    constexpr int kAccBytes = SLOTS * G * D * 4;
+    constexpr int kStageBytes = MF ? kWaves * 4 * kBS * C::ROW : 0;
     __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[2 * kWaves][G];
-    __shared__ float s_acc[2 * kWaves][G * D];
+    __shared__ float s_l[SLOTS][G];
+    __shared__ __align__(16) uint8_t s_raw[kAccBytes > kStageBytes ? kAccBytes : kStageBytes];
+    float(*s_acc)[G * D] = reinterpret_cast<float(*)[G * D]>(s_raw);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -563,7 +645,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             if (s_old != (uint32_t)(ns - 1)) return;
             const float* rec0 =
                 a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
-            merge_in_workgroup<D, G>(rec0, (int)ns, a.rec_floats, a.out, a.out_kind, obase);
+            // the merge's LDS: the staging / partial-state memory, which no
+            // thread reads any more, where it is large enough
+            if constexpr (sizeof(MergeLds<D, G>) <= sizeof(s_raw)) {
+                merge_in_workgroup<D, G>(*reinterpret_cast<MergeLds<D, G>*>(s_raw), rec0, (int)ns,
+                                         a.rec_floats, a.out, a.out_kind, obase);
+            } else {
+                __shared__ MergeLds<D, G> s_merge;
+                merge_in_workgroup<D, G>(s_merge, rec0, (int)ns, a.rec_floats, a.out, a.out_kind,
+                                         obase);
+            }
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
@@ -616,28 +707,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         }
     }
 
-    // query chunks of the G heads of this group
-    Chunk qv[G][C::NC];
-    {
-        const int64_t qoff =
-            (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
-        const uint8_t* qb = a.q + qoff * C::EB;
-#pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int c = 0; c < C::NC; c++)
-                qv[h][c] = *reinterpret_cast<const Chunk*>(qb + (h * D) * C::EB + (c * C::LPG + r) * 16);
-    }
-
-    float m[G], l[G], acc[G][C::DPL];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        m[h] = kEmptyMax;
-        l[h] = 0.f;
-#pragma unroll
-        for (int i = 0; i < C::DPL; i++) acc[h][i] = 0.f;
-    }
-
     const uint64_t nblk_pool = a.n_pool_blocks;
     // physical block i of this wave.  Block 0 stands in for an id outside
     // the pool, so the loads stay in bounds; every block of a split holds
@@ -650,11 +719,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             (uint32_t)(lb0 + wave + (int64_t)i * kWaves) & ((1u << tpb_log2) - 1u);
         return a.pool + (uint64_t)(ok ? id : 0) * a.block_bytes + tile_in_block * (kBS * C::ROW);
     };
-    auto fold = [&](BlockRegs<T, D, G>& br, int i, bool ok) {
-        const int64_t lb = lb0 + wave + (int64_t)i * kWaves;
-        const int64_t first = lb * kBS;
+    // Appending modes: the new token's rows, from the arguments, replace the
+    // loaded rows of its tile (logical tile lb).
+    auto put_new_row = [&](BlockRegs<T, D, G>& br, int64_t lb) {
         if constexpr (APPENDS) {
-            if (new_here && lb == bZ) {  // the new token's row from the arguments
+            if (new_here && lb == bZ) {
                 const int row = (int)((L - 1) % kBS);
 #pragma unroll
                 for (int rho = 0; rho < C::ROWS; rho++) {
@@ -670,75 +739,308 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
                 }
             }
         }
-        if (ok && first >= lo && first + kBS <= L) {
-            process_block<T, D, G, true>(br, nullptr, qv, a.qk_scale_log2, m, l, acc);
-        } else {
-            bool valid[C::ROWS];
-#pragma unroll
-            for (int rho = 0; rho < C::ROWS; rho++) {
-                const int64_t pos = first + g + C::NG * rho;
-                valid[rho] = ok && pos >= lo && pos < L;
-            }
-            process_block<T, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
-            if (!ok) {  // an id outside the pool: NaN for every query head of the group
-#pragma unroll
-                for (int h = 0; h < G; h++) l[h] = __builtin_nanf("");
-            }
-        }
     };
 
-    // Two blocks per iteration: both blocks' loads (16 KiB per wave) are
-    // issued before either is folded in.
-    for (int i = 0; i < my_n; i += 2) {
-        BlockRegs<T, D, G> bufA, bufB;
-        bool okA, okB = false;
-        load_block<T, D, G>(bufA, block_ptr(i, okA), vofs, g, r);
-        if (i + 1 < my_n) load_block<T, D, G>(bufB, block_ptr(i + 1, okB), vofs, g, r);
-        fold(bufA, i, okA);
-        if (i + 1 < my_n) fold(bufB, i + 1, okB);
-    }
+    if constexpr (MF) {
+        // ---- MFMA block loop ----
+        // A wave takes its tiles in pairs.  The pair's K and V rows go from
+        // registers into the wave's own LDS staging area, then the loads of
+        // the next pair are issued into the same registers and the pair is
+        // folded in from LDS while they are in flight:
+        //   S^T = K Q^T     4 (head_dim / 128) 16x16x32 MFMAs per tile; column
+        //                   j of the 16 is query head j of the group (Q^T
+        //                   operand zero beyond G); lane l holds tokens
+        //                   4 (l / 16) .. + 3 of column l % 16;
+        //   O^T += V^T P^T  one 16x16x32 MFMA per 16 rows of O^T and P part;
+        //                   the 32 keys of the pair are ordered so that the
+        //                   S^T registers of the two tiles are the B operand
+        //                   as they stand, and V^T comes from transposing
+        //                   LDS reads.
+        // P = 2^(s - m) enters the products in parts that sum to it almost
+        // exactly: for bf16 caches a truncated high part, a truncated middle
+        // part and the rounded rest (relative error below 2^-22); for fp16
+        // caches the fp16 value of P 2^15 and its rounded remainder (P 2^15
+        // stays in fp16's normal range down to P = 2^-29; the 2^15 is taken
+        // out of the accumulator at the end).  l sums P in fp32.
+        typedef MfmaCfg<D> F;
+        const int col = lane & 15;  // S^T and O^T column (query head of the group)
+        const int g16 = lane >> 4;  // output rows 4 g16 .. + 3 of each 16-row tile
+        u32x4 qop[F::KSTEP];        // Q^T: dims 32 s + 8 g16 .. + 7 of head col
+        {
+            const int64_t qoff =
+                (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
+            const uint8_t* qrow = a.q + (qoff + (int64_t)(col < G ? col : 0) * D) * 2;
+#pragma unroll
+            for (int s = 0; s < F::KSTEP; s++)
+                qop[s] = col < G ? *reinterpret_cast<const u32x4*>(qrow + (32 * s + 8 * g16) * 2)
+                                 : u32x4{0, 0, 0, 0};
+        }
+        f32x4 oacc[F::DT];
+#pragma unroll
+        for (int t = 0; t < F::DT; t++) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = kEmptyMax, l = 0.f;  // state of column col (same in the 4 lane groups)
 
-    // ---- merge the 32 group states of the workgroup, in a fixed order ----
+        // staging area of this wave: K and V rows of tile 0, then of tile 1
+        uint8_t* const stage = s_raw + wave * (4 * F::TILE);
+        uint32_t koff[F::KSTEP];  // K operand of k-step s: row col, chunk 4 s + g16
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        float M = m[h];
-        if constexpr (C::LPG <= 8) M = fmaxf(M, xor8(M));
-        if constexpr (C::LPG <= 16) M = fmaxf(M, xor16(M));
-        M = fmaxf(M, xor32(M));
-        if (lane == 0) s_m[wave][h] = M;
-    }
-    __syncthreads();
+        for (int s = 0; s < F::KSTEP; s++)
+            koff[s] = (uint32_t)(col * C::ROW + (((4 * s + g16) ^ F::swz(col)) * 16));
+        // V^T operand of rows 16 t .. + 15 of O^T: this lane's transposing
+        // read covers row 4 g16 + col / 4, dims 16 t + 4 (col % 4) .. + 3
+        const int vrow = 4 * g16 + (col >> 2);
+        uint32_t voff[F::DT];
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        float MW = s_m[0][h];
+        for (int t = 0; t < F::DT; t++)
+            voff[t] = (uint32_t)(vrow * C::ROW +
+                                 (((2 * t + ((col & 3) >> 1)) ^ F::swz(vrow)) * 16) + (col & 1) * 8);
+
+        // rows of a loaded tile into the staging area; V rows outside the
+        // window (all rows when the block id was outside the pool) are
+        // written as zeros, so that stale pool bytes cannot enter as NaN * 0
+        auto stage_put = [&](const BlockRegs<T, D, G>& br, int tau, int64_t lb, bool ok) {
+            uint8_t* kst = stage + tau * 2 * F::TILE;
+            uint8_t* vst = kst + F::TILE;
+            const int64_t first = lb * kBS;
+            const bool full = ok && first >= lo && first + kBS <= L;
 #pragma unroll
-        for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
-        const float f = fast_exp2(m[h] - MW);
-        float lh = l[h] * f;
-        if constexpr (C::LPG <= 8) lh += xor8(lh);
-        if constexpr (C::LPG <= 16) lh += xor16(lh);
+            for (int rho = 0; rho < C::ROWS; rho++) {
+                const int row = g + C::NG * rho;
+                const bool keep = full || (ok && first + row >= lo && first + row < L);
 #pragma unroll
-        for (int i = 0; i < C::DPL; i++) {
-            float x = acc[h][i] * f;
-            if constexpr (C::LPG <= 8) x += xor8(x);
-            if constexpr (C::LPG <= 16) x += xor16(x);
-            acc[h][i] = x;
+                for (int c = 0; c < C::NC; c++) {
+                    const uint32_t off =
+                        (uint32_t)(row * C::ROW + (((c * C::LPG + r) ^ F::swz(row)) * 16));
+                    *reinterpret_cast<Chunk*>(kst + off) = br.k[rho][c];
+                    *reinterpret_cast<Chunk*>(vst + off) = keep ? br.v[rho][c] : Chunk{};
+                }
+            }
+        };
+        auto stage_zero_v = [&](int tau) {  // V rows of a tile the pair does not have
+            uint8_t* vst = stage + tau * 2 * F::TILE + F::TILE;
+#pragma unroll
+            for (int c = 0; c < F::TILE / (64 * 16); c++)
+                *reinterpret_cast<u32x4*>(vst + (c * 64 + lane) * 16) = u32x4{0, 0, 0, 0};
+        };
+        auto scores = [&](int tau) -> f32x4 {
+            const uint8_t* kst = stage + tau * 2 * F::TILE;
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < F::KSTEP; k++)
+                s = mfma16<T>(*reinterpret_cast<const u32x4*>(kst + koff[k]), qop[k], s);
+            return s;
+        };
+        // fold the staged pair (tiles i and i + 1 of this wave) into the state
+        auto fold_pair = [&](int i, bool okA, bool okB, bool hasB) {
+            const int64_t pA = (lb0 + wave + (int64_t)i * kWaves) * kBS + 4 * g16;
+            const int64_t pB = pA + kWaves * kBS;
+            const f32x4 sA = scores(0), sB = scores(1);
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                sv[e] = (okA && pA + e >= lo && pA + e < L) ? sA[e] * a.qk_scale_log2 : -INFINITY;
+                sv[4 + e] = (hasB && okB && pB + e >= lo && pB + e < L)
+                                ? sB[e] * a.qk_scale_log2
+                                : -INFINITY;
+            }
+            float mx = sv[0];
+#pragma unroll
+            for (int e = 1; e < 8; e++) mx = fmaxf(mx, sv[e]);
+            mx = fmaxf(mx, xor16(mx));
+            mx = fmaxf(mx, xor32(mx));
+            if (__builtin_amdgcn_ballot_w64(mx > m)) {  // rare once the maxima have settled
+                const float mn = fmaxf(m, mx);
+                const float alpha = fast_exp2(m - mn);
+                l *= alpha;
+#pragma unroll
+                for (int t = 0; t < F::DT; t++) oacc[t] *= alpha;
+                m = mn;
+            }
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                p[e] = fast_exp2(sv[e] - m);
+                l += p[e];
+            }
+            u32x4 part[3];
+            constexpr int NP = T == kF16 ? 2 : 3;
+            if constexpr (T == kF16) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const float x0 = p[2 * q] * 32768.f, x1 = p[2 * q + 1] * 32768.f;
+                    hw[q] = pack_f16_rne(x0, x1);
+                    const f16x2_t h = __builtin_bit_cast(f16x2_t, hw[q]);
+                    lw[q] = pack_f16_rne(x0 - (float)h.x, x1 - (float)h.y);
+                }
+                part[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                part[1] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            } else {
+                uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const float x0 = p[2 * q], x1 = p[2 * q + 1];
+                    hw[q] = pack_bf16_trunc(x0, x1);
+                    const float r0 = x0 - bf16_lo(hw[q]), r1 = x1 - bf16_hi(hw[q]);
+                    mw[q] = pack_bf16_trunc(r0, r1);
+                    lw[q] = pack_bf16_rne(r0 - bf16_lo(mw[q]), r1 - bf16_hi(mw[q]));
+                }
+                part[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                part[1] = u32x4{mw[0], mw[1], mw[2], mw[3]};
+                part[2] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            }
+#pragma unroll
+            for (int t = 0; t < F::DT; t++) {
+                const u32x2 v0 = tr_read(stage + F::TILE + voff[t]);
+                const u32x2 v1 = tr_read(stage + 3 * F::TILE + voff[t]);
+                const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+                for (int k = 0; k < NP; k++) oacc[t] = mfma16<T>(va, part[k], oacc[t]);
+            }
+            if (!okA || (hasB && !okB)) l = __builtin_nanf("");  // an id outside the pool
+        };
+
+        BlockRegs<T, D, G> bufA, bufB;
+        bool okA = false, okB = false;
+        if (my_n > 0) load_block<T, D, G>(bufA, block_ptr(0, okA), vofs, g, r);
+        if (my_n > 1) load_block<T, D, G>(bufB, block_ptr(1, okB), vofs, g, r);
+        for (int i = 0; i < my_n; i += 2) {
+            const bool hasB = i + 1 < my_n;
+            const int64_t lbA = lb0 + wave + (int64_t)i * kWaves;
+            wave_lds_order();  // after the previous pair's LDS reads
+            put_new_row(bufA, lbA);
+            stage_put(bufA, 0, lbA, okA);
+            if (hasB) {
+                put_new_row(bufB, lbA + kWaves);
+                stage_put(bufB, 1, lbA + kWaves, okB);
+            } else {
+                stage_zero_v(1);
+            }
+            wave_lds_order();
+            const bool curA = okA, curB = okB;
+            if (i + 2 < my_n) load_block<T, D, G>(bufA, block_ptr(i + 2, okA), vofs, g, r);
+            if (i + 3 < my_n) load_block<T, D, G>(bufB, block_ptr(i + 3, okB), vofs, g, r);
+            fold_pair(i, curA, curB, hasB);
         }
-        if ((lane & 31) < C::LPG) {  // the first group of each half wave holds its sums
-            const int sl = wave * 2 + (lane >> 5);
+
+        // ---- merge the 4 wave states of the workgroup, in a fixed order ----
+        if (lane < G) s_m[wave][lane] = m;
+        __syncthreads();  // every wave has also left its loop: s_acc may reuse the staging
+        const int hq = col < G ? col : 0;
+        float MW = s_m[0][hq];
 #pragma unroll
-            for (int c = 0; c < C::NC; c++)
+        for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][hq]);
+        const float f = fast_exp2(m - MW);
+        const float fo = T == kF16 ? f * (1.f / 32768.f) : f;
+        float lh = l * f;
+        lh += xor16(lh);
+        lh += xor32(lh);
+        if (col < G) {
 #pragma unroll
-                for (int e = 0; e < C::EPC; e++)
-                    s_acc[sl][h * D + (c * C::LPG + r) * C::EPC + e] = acc[h][c * C::EPC + e];
-            if (r == 0) s_l[sl][h] = lh;
+            for (int t = 0; t < F::DT; t++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) s_acc[wave][col * D + 16 * t + 4 * g16 + e] = oacc[t][e] * fo;
         }
+        if (lane < G) s_l[wave][lane] = lh;
+        __syncthreads();
+    } else {
+        // ---- per-lane block loop ----
+        // query chunks of the G heads of this group
+        Chunk qv[G][C::NC];
+        {
+            const int64_t qoff =
+                (((int64_t)rel_layer * a.n_seqs + b) * a.n_q_heads + (int64_t)hd.head * G) * D;
+            const uint8_t* qb = a.q + qoff * C::EB;
+#pragma unroll
+            for (int h = 0; h < G; h++)
+#pragma unroll
+                for (int c = 0; c < C::NC; c++)
+                    qv[h][c] = *reinterpret_cast<const Chunk*>(qb + (h * D) * C::EB + (c * C::LPG + r) * 16);
+        }
+
+        float m[G], l[G], acc[G][C::DPL];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            m[h] = kEmptyMax;
+            l[h] = 0.f;
+#pragma unroll
+            for (int i = 0; i < C::DPL; i++) acc[h][i] = 0.f;
+        }
+
+        auto fold = [&](BlockRegs<T, D, G>& br, int i, bool ok) {
+            const int64_t lb = lb0 + wave + (int64_t)i * kWaves;
+            const int64_t first = lb * kBS;
+            put_new_row(br, lb);
+            if (ok && first >= lo && first + kBS <= L) {
+                process_block<T, D, G, true>(br, nullptr, qv, a.qk_scale_log2, m, l, acc);
+            } else {
+                bool valid[C::ROWS];
+#pragma unroll
+                for (int rho = 0; rho < C::ROWS; rho++) {
+                    const int64_t pos = first + g + C::NG * rho;
+                    valid[rho] = ok && pos >= lo && pos < L;
+                }
+                process_block<T, D, G, false>(br, valid, qv, a.qk_scale_log2, m, l, acc);
+                if (!ok) {  // an id outside the pool: NaN for every query head of the group
+#pragma unroll
+                    for (int h = 0; h < G; h++) l[h] = __builtin_nanf("");
+                }
+            }
+        };
+
+        // Two blocks per iteration: both blocks' loads (16 KiB per wave) are
+        // issued before either is folded in.
+        for (int i = 0; i < my_n; i += 2) {
+            BlockRegs<T, D, G> bufA, bufB;
+            bool okA, okB = false;
+            load_block<T, D, G>(bufA, block_ptr(i, okA), vofs, g, r);
+            if (i + 1 < my_n) load_block<T, D, G>(bufB, block_ptr(i + 1, okB), vofs, g, r);
+            fold(bufA, i, okA);
+            if (i + 1 < my_n) fold(bufB, i + 1, okB);
+        }
+
+        // ---- merge the 32 group states of the workgroup, in a fixed order ----
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float M = m[h];
+            if constexpr (C::LPG <= 8) M = fmaxf(M, xor8(M));
+            if constexpr (C::LPG <= 16) M = fmaxf(M, xor16(M));
+            M = fmaxf(M, xor32(M));
+            if (lane == 0) s_m[wave][h] = M;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float MW = s_m[0][h];
+#pragma unroll
+            for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
+            const float f = fast_exp2(m[h] - MW);
+            float lh = l[h] * f;
+            if constexpr (C::LPG <= 8) lh += xor8(lh);
+            if constexpr (C::LPG <= 16) lh += xor16(lh);
+#pragma unroll
+            for (int i = 0; i < C::DPL; i++) {
+                float x = acc[h][i] * f;
+                if constexpr (C::LPG <= 8) x += xor8(x);
+                if constexpr (C::LPG <= 16) x += xor16(x);
+                acc[h][i] = x;
+            }
+            if ((lane & 31) < C::LPG) {  // the first group of each half wave holds its sums
+                const int sl = wave * 2 + (lane >> 5);
+#pragma unroll
+                for (int c = 0; c < C::NC; c++)
+#pragma unroll
+                    for (int e = 0; e < C::EPC; e++)
+                        s_acc[sl][h * D + (c * C::LPG + r) * C::EPC + e] = acc[h][c * C::EPC + e];
+                if (r == 0) s_l[sl][h] = lh;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     for (int e = threadIdx.x; e < G * D; e += kThreads) {
         float sum = 0.f;
 #pragma unroll
-        for (int sl = 0; sl < 2 * kWaves; sl++) sum += s_acc[sl][e];
+        for (int sl = 0; sl < SLOTS; sl++) sum += s_acc[sl][e];
         rec_put(rec + e, sum, streamed);
     }
     if (threadIdx.x < G) {
@@ -748,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 #pragma unroll
         for (int w = 1; w < kWaves; w++) MW = fmaxf(MW, s_m[w][h]);
 #pragma unroll
-        for (int sl = 0; sl < 2 * kWaves; sl++) lsum += s_l[sl][h];
+        for (int sl = 0; sl < SLOTS; sl++) lsum += s_l[sl][h];
         rec_put(rec + G * D + h, MW, streamed);
         rec_put(rec + G * D + G + h, lsum, streamed);
     }
@@ -784,7 +1086,8 @@ __global__ __launch_bounds__((MergeCfg<D, G>::THREADS)) void decode_merge_kernel
     const int ns = (int)((n + a.split_tokens - 1) / a.split_tokens);
     const float* rec0 =
         a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
-    merge_chunks<D, G, M::THREADS>(rec0, ns, a.rec_floats, ds0, ds0 + a.merge_chunks, a.out,
+    __shared__ MergeLds<D, G> s_merge;
+    merge_chunks<D, G, M::THREADS>(s_merge, rec0, ns, a.rec_floats, ds0, ds0 + a.merge_chunks, a.out,
                                    a.out_kind, obase);
 }
 
