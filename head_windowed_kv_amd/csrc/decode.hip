@@ -8,22 +8,32 @@
 // of the window [max(0, L-w), L) (cut on block boundaries, the last split
 // taking the remainder); the workgroup streams those K/V blocks through the
 // head's ring and keeps, for the G query heads of the GQA group, an
-// online-softmax state (running max m, sum l, weighted sum acc) in
-// registers.  Decode is HBM-bound (about 3 flop per byte read), so there
-// is no MFMA here: the design goal is to keep enough 128-bit loads in flight.
+// online-softmax state (running max m, sum l, weighted sum acc).  Decode is
+// HBM-bound (G flop per byte of 16-bit K/V read), so the design goal is to
+// keep enough 128-bit loads in flight and the per-byte arithmetic off the
+// critical path.
 //
 // Work layout inside a workgroup (256 threads = 4 wave64):
-//   - a wave processes one whole block (16 tokens x 256 B of K, same of V) at
-//     a time, blocks of the split interleaved over the 4 waves, two blocks in
+//   - a wave processes one 16-token tile (16 rows of K, same of V) at a
+//     time, tiles of the split interleaved over the 4 waves, two tiles in
 //     flight per wave;
-//   - the 64 lanes form 8 groups of 8; group g owns rows g and g+8 of the
-//     block, lane r of a group owns 16-byte chunks r and r+8 of each row, so
-//     every load instruction of the wave reads whole 128-byte lines;
-//   - q.k partial dots use v_dot2_f32_bf16 (bf16 products are exact in fp32)
-//     and are summed over the 8 lanes of a group with DPP;
-//   - each group keeps its own softmax state; states are merged across groups
-//     and waves once, at the end, in a fixed order (results do not depend on
-//     the batch composition or on timing).
+//   - loads: the 64 lanes form groups of 8 (32 for 512-byte rows); group g
+//     owns rows g, g+8 of the tile, lane r of a group 16-byte chunks r,
+//     r+8, ... of each row, so every load instruction reads whole 128-byte
+//     lines.
+// 16-bit caches (MFMA block loop): each wave writes its pair of tiles into
+// its own LDS staging area, issues the next pair's loads into the same
+// registers, and folds the pair in from LDS on the matrix cores: S^T = K Q^T
+// on 16x16x32 MFMAs (the 16 columns are the G query heads of the group,
+// padded), the online softmax on the S^T registers, O^T += V^T P^T with V^T
+// from transposing LDS reads (ds_read_b64_tr_b16) and P split into 16-bit
+// parts that sum to it within ~2^-22 (bf16: three parts; fp16: two parts
+// of P 2^15).  The per-byte VALU work then no longer grows with G.
+// fp32 caches (per-lane loop): q.k partial dots in fp32 FMAs summed over the
+// lanes of a group with DPP; each group keeps its own softmax state.
+// Either way the partial states are merged across lanes and waves once, at
+// the end, in a fixed order (results do not depend on the batch
+// composition or on timing).
 //
 // Stage 2 (merge): per (layer, sequence, kv head), combine the splits:
 //   M = max_s m_s;  o = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
@@ -228,8 +238,11 @@ struct SplitCfg {
 // (16-bit caches).  In the per-lane form the VALU work per byte grows with G
 // (a dot product and a multiply-add per element and query head) and bounds
 // the kernel from G = 4 on; the matrix cores handle a 16-column S^T tile
-// whatever G <= 16 is.
-constexpr int kMfmaMinGroup = 4;
+// whatever G <= 16 is.  At G = 1-3 the MFMA loop streams as fast (head_dim
+// 64 / 128) or faster (head_dim 256: the per-lane form runs one wave per
+// SIMD there), and its shorter epilogue helps small launches, so every
+// 16-bit cache takes it; fp32 caches keep the per-lane form.
+constexpr int kMfmaMinGroup = 1;
 
 // Geometry of the MFMA block loop for head_dim D (16-bit elements).
 template <int D>
