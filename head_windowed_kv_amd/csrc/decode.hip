@@ -756,10 +756,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 
     if constexpr (MF) {
         // ---- MFMA block loop ----
-        // A wave takes its tiles in pairs.  The pair's K and V rows go from
-        // registers into the wave's own LDS staging area, then the loads of
-        // the next pair are issued into the same registers and the pair is
-        // folded in from LDS while they are in flight:
+        // A wave takes its tiles in pairs.  Each tile's K and V rows go from
+        // registers into the wave's own LDS staging area, and the load of the
+        // tile two ahead is issued into the same registers at once; the pair
+        // is then folded in from LDS while those loads are in flight:
         //   S^T = K Q^T     4 (head_dim / 128) 16x16x32 MFMAs per tile; column
         //                   j of the 16 is query head j of the group (Q^T
         //                   operand zero beyond G); lane l holds tokens
@@ -921,18 +921,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             const bool hasB = i + 1 < my_n;
             const int64_t lbA = lb0 + wave + (int64_t)i * kWaves;
             wave_lds_order();  // after the previous pair's LDS reads
+            const bool curA = okA, curB = okB;
             put_new_row(bufA, lbA);
-            stage_put(bufA, 0, lbA, okA);
+            stage_put(bufA, 0, lbA, curA);
+            if (i + 2 < my_n) load_block<T, D, G>(bufA, block_ptr(i + 2, okA), vofs, g, r);
             if (hasB) {
                 put_new_row(bufB, lbA + kWaves);
-                stage_put(bufB, 1, lbA + kWaves, okB);
+                stage_put(bufB, 1, lbA + kWaves, curB);
             } else {
                 stage_zero_v(1);
             }
-            wave_lds_order();
-            const bool curA = okA, curB = okB;
-            if (i + 2 < my_n) load_block<T, D, G>(bufA, block_ptr(i + 2, okA), vofs, g, r);
             if (i + 3 < my_n) load_block<T, D, G>(bufB, block_ptr(i + 3, okB), vofs, g, r);
+            wave_lds_order();
             fold_pair(i, curA, curB, hasB);
         }
 
