@@ -114,22 +114,6 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
-                                  false);
-}
-__device__ __forceinline__ float f16_lo(uint32_t w) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-}
-__device__ __forceinline__ float f16_hi(uint32_t w) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int CTRL>
@@ -234,15 +218,17 @@ struct SplitCfg {
     static_assert(NC >= 1 && ROW % (16 * LPG) == 0, "rows of whole lane chunks");
 };
 
-// GQA groups of at least this many query heads take the MFMA block loop
-// (16-bit caches).  In the per-lane form the VALU work per byte grows with G
-// (a dot product and a multiply-add per element and query head) and bounds
-// the kernel from G = 4 on; the matrix cores handle a 16-column S^T tile
+// Which loop a cache takes.  In the per-lane form the VALU work per byte
+// grows with the GQA group G (a dot product and a multiply-add per element
+// and query head) and bounds the kernel from G = 4 on (2.1 TB/s at G = 8 on
+// the 48-layer 112K stack); the matrix cores handle a 16-column S^T tile
 // whatever G <= 16 is.  At G = 1-3 the MFMA loop streams as fast (head_dim
-// 64 / 128) or faster (head_dim 256: the per-lane form runs one wave per
-// SIMD there), and its shorter epilogue helps small launches, so every
-// 16-bit cache takes it; fp32 caches keep the per-lane form.
-constexpr int kMfmaMinGroup = 1;
+// 64 / 128) or faster (head_dim 256, where the per-lane form runs one wave
+// per SIMD), and its shorter epilogue helps small launches, so every 16-bit
+// cache takes it; fp32 caches (no fp32-exact 16-bit operands) keep the
+// per-lane form.
+template <int T>
+constexpr bool mfma_loop() { return T != kF32; }
 
 // Geometry of the MFMA block loop for head_dim D (16-bit elements).
 template <int D>
@@ -255,50 +241,27 @@ struct MfmaCfg {
     static __device__ __forceinline__ int swz(int t) { return t & (CPR < 16 ? CPR - 1 : 15); }
 };
 
-// partial dot product of one row chunk with one query chunk (16-bit
-// products are exact in fp32 and accumulated in fp32)
+// Per-lane loop (fp32 caches): partial dot product of one row chunk with one
+// query chunk, and element e of a chunk.
 template <int T>
 __device__ __forceinline__ float chunk_dot(const typename Elem<T>::Chunk& q,
                                            const typename Elem<T>::Chunk& k, float acc) {
-    if constexpr (T == kF32) {
-        acc = fmaf(q.x, k.x, acc);
-        acc = fmaf(q.y, k.y, acc);
-        acc = fmaf(q.z, k.z, acc);
-        acc = fmaf(q.w, k.w, acc);
-    } else if constexpr (T == kBF16) {
-        acc = dot2_bf16(q.x, k.x, acc);
-        acc = dot2_bf16(q.y, k.y, acc);
-        acc = dot2_bf16(q.z, k.z, acc);
-        acc = dot2_bf16(q.w, k.w, acc);
-    } else {
-        acc = dot2_f16(q.x, k.x, acc);
-        acc = dot2_f16(q.y, k.y, acc);
-        acc = dot2_f16(q.z, k.z, acc);
-        acc = dot2_f16(q.w, k.w, acc);
-    }
+    static_assert(T == kF32, "the per-lane loop serves fp32 caches");
+    acc = fmaf(q.x, k.x, acc);
+    acc = fmaf(q.y, k.y, acc);
+    acc = fmaf(q.z, k.z, acc);
+    acc = fmaf(q.w, k.w, acc);
     return acc;
 }
 
-// widen element e of a chunk to fp32
 template <int T>
 __device__ __forceinline__ float chunk_elem(const typename Elem<T>::Chunk& v, int e) {
-    if constexpr (T == kF32) {
-        switch (e) {
-            case 0: return v.x;
-            case 1: return v.y;
-            case 2: return v.z;
-            default: return v.w;
-        }
-    } else {
-        uint32_t w;
-        switch (e >> 1) {
-            case 0: w = v.x; break;
-            case 1: w = v.y; break;
-            case 2: w = v.z; break;
-            default: w = v.w; break;
-        }
-        if constexpr (T == kBF16) return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-        return (e & 1) ? f16_hi(w) : f16_lo(w);
+    static_assert(T == kF32, "the per-lane loop serves fp32 caches");
+    switch (e) {
+        case 0: return v.x;
+        case 1: return v.y;
+        case 2: return v.z;
+        default: return v.w;
     }
 }
 
@@ -569,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     typedef typename Elem<T>::Chunk Chunk;
     constexpr bool FUSED = MODE == kModeFused;     // merges in the last split
     constexpr bool APPENDS = MODE != kModePlain;  // ctx_len holds positions; appends
-    constexpr bool MF = T != kF32 && G >= kMfmaMinGroup;  // MFMA block loop
+    constexpr bool MF = mfma_loop<T>();  // MFMA block loop
     static_assert(!MF || G <= 16, "one 16-column S^T tile per GQA group");
     // Partial states the workgroup merge adds up: one per half wave in the
     // per-lane form, one per wave in the MFMA form.  The MFMA form stages the
@@ -733,20 +696,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         return a.pool + (uint64_t)(ok ? id : 0) * a.block_bytes + tile_in_block * (kBS * C::ROW);
     };
     // Appending modes: the new token's rows, from the arguments, replace the
-    // loaded rows of its tile (logical tile lb).
+    // loaded rows of its tile (logical tile lb).  This lane's chunks of them
+    // are read once, before the block loop: a load inside the loop would make
+    // its wait (the wait counter is in order) drain the tile loads issued
+    // before it.
+    const int new_row = (int)((L - 1) % kBS);
+    const bool new_lane = new_here && (new_row - g) % C::NG == 0;  // lane holds that row
+    Chunk nk[C::NC], nv[C::NC];
+    if constexpr (APPENDS) {
+        if (new_lane) {
+#pragma unroll
+            for (int c = 0; c < C::NC; c++) {
+                nk[c] = *reinterpret_cast<const Chunk*>(a.k_new + kv_new_off + (c * C::LPG + r) * 16);
+                nv[c] = *reinterpret_cast<const Chunk*>(a.v_new + kv_new_off + (c * C::LPG + r) * 16);
+            }
+        }
+    }
     auto put_new_row = [&](BlockRegs<T, D, G>& br, int64_t lb) {
         if constexpr (APPENDS) {
-            if (new_here && lb == bZ) {
-                const int row = (int)((L - 1) % kBS);
+            if (new_lane && lb == bZ) {
 #pragma unroll
                 for (int rho = 0; rho < C::ROWS; rho++) {
-                    if (g + C::NG * rho == row) {
+                    if (g + C::NG * rho == new_row) {
 #pragma unroll
                         for (int c = 0; c < C::NC; c++) {
-                            br.k[rho][c] = *reinterpret_cast<const Chunk*>(
-                                a.k_new + kv_new_off + (c * C::LPG + r) * 16);
-                            br.v[rho][c] = *reinterpret_cast<const Chunk*>(
-                                a.v_new + kv_new_off + (c * C::LPG + r) * 16);
+                            br.k[rho][c] = nk[c];
+                            br.v[rho][c] = nv[c];
                         }
                     }
                 }
