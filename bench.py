@@ -52,9 +52,9 @@ def parse():
                    help="run only the 161K chunked-prefill leg (e.g. under rocprofv3 --pmc)")
     p.add_argument("--no-mixed", action="store_true",
                    help="skip the mixed-stack leg (fp16 / 64-token blocks, hybrid SWA + "
-                        "global stack, head_dim 256 prefill)")
+                        "global stack, head_dim 256 prefill) and the GQA-group leg")
     p.add_argument("--mixed-only", action="store_true",
-                   help="run only the mixed-stack leg (e.g. under rocprofv3)")
+                   help="run only the mixed-stack and GQA-group legs (e.g. under rocprofv3)")
     p.add_argument("--single-layer-only", action="store_true",
                    help="run only the one-layer, 8-sequence, 32K-context decode leg (e.g. "
                         "under rocprofv3)")
@@ -253,7 +253,8 @@ def main():
         import head_windowed_kv_amd as H
         import synth
         torch.cuda.set_device(0)
-        print(json.dumps({"mixed_stacks": mixed_leg(H, torch, synth)}), flush=True)
+        print(json.dumps({"mixed_stacks": mixed_leg(H, torch, synth),
+                          "gqa_groups": gqa_leg(H, torch, synth)}), flush=True)
         return
     if args.single_layer_only:
         import torch
@@ -445,6 +446,8 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_mixed:
             result["mixed_stacks"] = mixed_leg(H, torch, synth)
+            torch.cuda.empty_cache()
+            result["gqa_groups"] = gqa_leg(H, torch, synth)
     if not args.no_cb:
         torch.cuda.empty_cache()
         result["continuous_batch_32seq"] = cb_leg(args, H, torch, synth)
@@ -786,16 +789,16 @@ def per_layer_graph(H, torch, cache, lay, windows, q, k_new, v_new, L, n_seqs, n
 
 
 def stack_decode_time(H, torch, synth, windows, dtype, block_size, L0, steps=20, n_warm=10,
-                      seed=0):
+                      seed=0, G=3, d=128):
     """One decode step per call over a whole stack (batch 1): the appending
     split + merge for all layers (hwkv_decode_append_attn, bf16 outputs),
     after filling each layer with the last min(L0, capacity) positions of
-    N(0,1) history; `n_warm` untimed steps, then `steps` timed as one block."""
+    N(0,1) history; `n_warm` untimed steps, then `steps` timed as one block.
+    G query heads per KV head, head_dim d."""
     import numpy as np
     dev = torch.device("cuda", 0)
     windows = np.asarray(windows, np.int32)
     n_layers, n_kv = windows.shape
-    G, d = 3, 128
     lay = H.hwkv_layout_create(windows, block_size, d, dtype)
     cache = H.make_cache(lay, 1, device=dev)
     cap = int(((windows.astype(np.int64) + block_size - 1) // block_size * block_size).max())
@@ -826,8 +829,7 @@ def stack_decode_time(H, torch, synth, windows, dtype, block_size, L0, steps=20,
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    b = float(np.minimum(windows.astype(np.int64), L0 + n_warm + steps // 2).sum()) * \
-        KV_BYTES_PER_TOK_HEAD
+    b = float(np.minimum(windows.astype(np.int64), L0 + n_warm + steps // 2).sum()) * 4 * d
     del cache, ws
     torch.cuda.empty_cache()
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(1.0 / (ms / 1e3), 1),
@@ -906,6 +908,21 @@ def mixed_leg(H, torch, synth):
     res["prefill_161k_head_dim256"]["workload"] = (
         "the 161K chunk of prefill_161k (4 seqs, 2048 rows at P=164864, layer-0 windows, 8x3 "
         "heads, bf16) at head_dim 256")
+    return res
+
+
+def gqa_leg(H, torch, synth):
+    """The headline's 48-layer stack (windows of seed 0, context 112K,
+    batch 1, bf16, 16-token blocks) with larger GQA groups: 8 query heads
+    per KV head at head_dim 128 and 256, 4 at head_dim 128."""
+    L0 = synth.CTX_112K
+    res = {}
+    for G, d in ((4, 128), (8, 128), (8, 256)):
+        r = stack_decode_time(H, torch, synth, synth.stack_windows(48, 8, 0), torch.bfloat16, 16,
+                              L0, seed=113, G=G, d=d)
+        r["workload"] = ("48 layers x 8 KV heads x %d query heads each, d=%d, bf16, windows of "
+                         "the headline (seed 0), context 112K, batch 1" % (G, d))
+        res["stack48_g%d_d%d" % (G, d)] = r
     return res
 
 
