@@ -14,9 +14,9 @@ import pytest
 import torch
 
 import synth
-from _gpu_common import (build_decode_case, build_stack_case, device, hw, oracle_decode,
-                         row_rel_err, run_decode_step, say, stack_oracle_layer, stack_step,
-                         to_host_f64, tol)
+from _gpu_common import (DECODE_REGRESSION_TOL, build_decode_case, build_stack_case, device, hw,
+                         oracle_decode, row_rel_err, run_decode_step, say, stack_oracle_layer,
+                         stack_step, to_host_f64, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,5 +175,37 @@ def test_mixed_stack_configs_at_full_size(kind):
     o16 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
     H.hwkv_decode_append_attn(c.cache, 0, 48, torch.tensor([synth.CTX_112K], device=dev),
                               c.k_new, c.v_new, c.q, 1.0 / math.sqrt(128), ws, o16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, out.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("group,head_dim", [(4, 128), (8, 128), (8, 256)])
+def test_gqa_stacks_at_full_size(group, head_dim):
+    """The GQA-group configurations the benchmark times, at full size: the
+    headline's 48-layer stack (windows of seed 0, context 112K, batch 1, bf16)
+    with 4 or 8 query heads per KV head.  Sampled layers against the oracle,
+    within the decode regression bound; the benchmark's launch (appending
+    split + merge, bf16 output) equals the three-launch step's fp32 results
+    rounded to bf16."""
+    H = hw()
+    dev = device()
+    windows = synth.stack_windows(48, 8, 0)
+    n_q = 8 * group
+    say("gqa stack G", group, "d", head_dim, ": fill")
+    c = build_stack_case(windows, torch.bfloat16, head_dim, group, synth.CTX_112K, 1, seed=707)
+    say("gqa stack G", group, "d", head_dim, ": step")
+    out = stack_step(c)
+    got = to_host_f64(out)
+    assert np.all(np.isfinite(got))
+    worst = 0.0
+    for l in (0, 29, 47):
+        worst = max(worst, row_rel_err(got[l:l + 1], stack_oracle_layer(c, l)))
+    say("gqa stack G", group, "d", head_dim, "max row rel err (sampled layers)", worst)
+    assert worst <= tol(torch.bfloat16)
+    assert worst <= DECODE_REGRESSION_TOL, worst
+    ws = H.make_workspace(c.lay, 0, 48, 1, n_q, device=dev)
+    o16 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
+    H.hwkv_decode_append_attn(c.cache, 0, 48, torch.tensor([synth.CTX_112K], device=dev),
+                              c.k_new, c.v_new, c.q, 1.0 / math.sqrt(head_dim), ws, o16)
     torch.cuda.synchronize()
     assert torch.equal(o16, out.to(torch.bfloat16))
