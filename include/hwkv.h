@@ -260,7 +260,10 @@ hwkv_status hwkv_append(const hwkv_layout *layout, const hwkv_cache *cache,
  * n_kv_heads query heads of the group (query head i reads kv head i / G),
  * s_t = log2(e) * scale * q_i . k_t.  q: device [n_layers][n_seqs][n_q_heads]
  * [head_dim] in the layout's dtype.  workspace: hwkv_workspace_bytes.
- * scale: finite and > 0. */
+ * scale: finite and > 0.  Arithmetic: q . k sums exact products in fp32;
+ * for 16-bit caches the weights 2^(s_t - m) enter acc as 16-bit parts that
+ * sum to them within ~2^-22 relative (matrix-core products, fp32
+ * accumulation), for fp32 caches as fp32. */
 hwkv_status hwkv_decode_split(const hwkv_layout *layout, const hwkv_cache *cache,
                               int32_t layer_begin, int32_t n_layers,
                               int32_t n_seqs, const int32_t *seq_slots,
