@@ -76,11 +76,40 @@ def parse():
     return p.parse_args()
 
 
+def code_tokens(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so
+    that a hash of it changes with the code, not with its comments or
+    layout (string and character literals are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # literal: copy through its closing quote
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the decode kernel's code (decode.hip and the shared header,
+    comments and layout ignored): committed counter summaries are reported
+    only while it matches the one they were taken on."""
     h = hashlib.sha256()
     for f in ("decode.hip", "hwkv_internal.h"):
-        with open(os.path.join(ROOT, "head_windowed_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "head_windowed_kv_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -735,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         // registers into the wave's own LDS staging area, and the load of the
         // tile two ahead is issued into the same registers at once; the pair
         // is then folded in from LDS while those loads are in flight:
-        //   S^T = K Q^T     4 (head_dim / 128) 16x16x32 MFMAs per tile; column
+        //   S^T = K Q^T     head_dim / 32 16x16x32 MFMAs per tile; column
         //                   j of the 16 is query head j of the group (Q^T
         //                   operand zero beyond G); lane l holds tokens
         //                   4 (l / 16) .. + 3 of column l % 16;
