@@ -68,6 +68,33 @@ def test_instances(dtype, d, G):
     _check(c, out)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8])
+def test_mfma_loop_every_instance(dtype, d, G):
+    """Every 16-bit decode instance (the MFMA block loop) against the oracle:
+    windows whose tiles leave waves with odd and even tile counts, one of 1
+    token, a partial last block and a partial first block; the pool starts as
+    NaN bytes, so any row outside a window that reached a product would
+    show."""
+    windows = [[1, 47, 700], [2100, 16, 333]]
+    say("mfma instance", dtype, d, G)
+    c = build_decode_case(windows, dtype, d, G, [5, 901, 2500], seed=304, split_tokens=256)
+    out = run_decode_step(c)
+    _check(c, out)
+
+
+@pytest.mark.parametrize("d,G", [(128, 6), (128, 8), (64, 6)])
+def test_fp32_large_groups(d, G):
+    """fp32 caches keep the per-lane loop; its large-group instances hold
+    more than 256 registers per lane (values parked in AGPRs)."""
+    windows = [[40, 700, 1], [2100, 16, 333]]
+    say("fp32 instance", d, G)
+    c = build_decode_case(windows, torch.float32, d, G, [5, 900, 2500], seed=305, split_tokens=256)
+    out = run_decode_step(c)
+    _check(c, out)
+
+
 def test_layer_subrange_and_scale():
     windows = [[64, 128], [300, 16], [1000, 5], [77, 4000]]
     say("layer subrange")
