@@ -137,9 +137,10 @@ def load_traffic(split_tokens: int, workload: str = "stack48"):
 
 PROBE_COPY_BYTES = 1 << 30
 # decode split length of the one-layer, 8-sequence, 32K leg: the fastest for
-# that workload in a sweep of 256-2048 tokens (0.1187 ms against 0.122 ms at
-# the default 1024)
-SINGLE_LAYER_SPLIT = 1536
+# that workload in a sweep of 1024-2048 tokens (its 672 streaming workgroups
+# then fit the 768 resident slots at once: 0.116-0.120 ms against 0.121-0.126
+# at the default 1024)
+SINGLE_LAYER_SPLIT = 2048
 
 
 def probe_lib():

@@ -526,8 +526,17 @@ __device__ void merge_in_workgroup(MergeLds<D, G>& sm, const float* rec0, int ns
 // and merges by the last-arriving split (hwkv_decode_step).
 constexpr int kModePlain = 0, kModeAppend = 1, kModeFused = 2;
 
+// Waves per SIMD the split kernel is built for (a lower bound on occupancy
+// the register allocation must allow): three for the MFMA loop up to
+// head_dim 128, whose staging takes 48 KiB of LDS per workgroup, so three
+// workgroups fit a CU (768 resident on the chip instead of 512); no bound
+// otherwise.
+template <int T, int D>
+constexpr int split_waves_per_simd() { return (mfma_loop<T>() && D <= 128) ? 3 : 1; }
+
 template <int T, int D, int G, int MODE>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<T, D>())))
+void decode_split_kernel(DecodeSplitArgs a) {
     typedef SplitCfg<T, D, G> C;
     typedef typename Elem<T>::Chunk Chunk;
     constexpr bool FUSED = MODE == kModeFused;     // merges in the last split
@@ -535,14 +544,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     constexpr bool MF = mfma_loop<T>();  // MFMA block loop
     static_assert(!MF || G <= 16, "one 16-column S^T tile per GQA group");
     // Partial states the workgroup merge adds up: one per half wave in the
-    // per-lane form, one per wave in the MFMA form.  The MFMA form stages the
-    // K and V rows of two tiles per wave in LDS; the merge reuses that memory
-    // once every wave has left its loop.
+    // per-lane form, one per wave in the MFMA form.  The MFMA form stages, per
+    // wave, the K rows of the tile being scored and the V rows of two tiles in
+    // LDS (48 KiB per workgroup at head_dim 128, so three workgroups fit a CU);
+    // the merge reuses that memory once every wave has left its loop.
     constexpr int SLOTS = MF ? kWaves : 2 * kWaves;
     constexpr int kAccBytes = SLOTS * G * D * 4;
-    constexpr int kStageBytes = MF ? kWaves * 4 * kBS * C::ROW : 0;
+    constexpr int kStageBytes = MF ? kWaves * 3 * kBS * C::ROW : 0;
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[SLOTS][G];
+    // appending modes: the new token's K and V rows, parked by the lanes of
+    // the wave whose tile holds it and read back by the same lanes
+    __shared__ __align__(16) uint8_t s_new[APPENDS ? 2 * C::ROW : 16];
     __shared__ __align__(16) uint8_t s_raw[kAccBytes > kStageBytes ? kAccBytes : kStageBytes];
     float(*s_acc)[G * D] = reinterpret_cast<float(*)[G * D]>(s_raw);
 
@@ -696,19 +709,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         return a.pool + (uint64_t)(ok ? id : 0) * a.block_bytes + tile_in_block * (kBS * C::ROW);
     };
     // Appending modes: the new token's rows, from the arguments, replace the
-    // loaded rows of its tile (logical tile lb).  This lane's chunks of them
-    // are read once, before the block loop: a load inside the loop would make
-    // its wait (the wait counter is in order) drain the tile loads issued
-    // before it.
+    // loaded rows of its tile (logical tile lb).  The lanes that hold them
+    // read their chunks once, before the block loop, and park them in LDS (a
+    // load inside the loop would make its wait, the wait counter being in
+    // order, drain the tile loads issued before it; registers would cost the
+    // third wave per SIMD).
     const int new_row = (int)((L - 1) % kBS);
-    const bool new_lane = new_here && (new_row - g) % C::NG == 0;  // lane holds that row
-    Chunk nk[C::NC], nv[C::NC];
+    // lane holds that row in the wave whose tiles include logical tile bZ
+    const bool new_lane = new_here && (new_row - g) % C::NG == 0 &&
+                          (int)((bZ - lb0) % kWaves) == wave;
     if constexpr (APPENDS) {
         if (new_lane) {
 #pragma unroll
             for (int c = 0; c < C::NC; c++) {
-                nk[c] = *reinterpret_cast<const Chunk*>(a.k_new + kv_new_off + (c * C::LPG + r) * 16);
-                nv[c] = *reinterpret_cast<const Chunk*>(a.v_new + kv_new_off + (c * C::LPG + r) * 16);
+                const int ch = (c * C::LPG + r) * 16;
+                *reinterpret_cast<Chunk*>(s_new + ch) =
+                    *reinterpret_cast<const Chunk*>(a.k_new + kv_new_off + ch);
+                *reinterpret_cast<Chunk*>(s_new + C::ROW + ch) =
+                    *reinterpret_cast<const Chunk*>(a.v_new + kv_new_off + ch);
             }
         }
     }
@@ -720,8 +738,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
                     if (g + C::NG * rho == new_row) {
 #pragma unroll
                         for (int c = 0; c < C::NC; c++) {
-                            br.k[rho][c] = nk[c];
-                            br.v[rho][c] = nv[c];
+                            const int ch = (c * C::LPG + r) * 16;
+                            br.k[rho][c] = *reinterpret_cast<const Chunk*>(s_new + ch);
+                            br.v[rho][c] = *reinterpret_cast<const Chunk*>(s_new + C::ROW + ch);
                         }
                     }
                 }
@@ -732,9 +751,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
     if constexpr (MF) {
         // ---- MFMA block loop ----
         // A wave takes its tiles in pairs.  Each tile's K and V rows go from
-        // registers into the wave's own LDS staging area, and the load of the
-        // tile two ahead is issued into the same registers at once; the pair
-        // is then folded in from LDS while those loads are in flight:
+        // registers into the wave's own LDS staging area (one K slot, scored
+        // before the next tile's K rows replace it; a V slot per tile), and
+        // the load of the tile two ahead is issued into the same registers at
+        // once; the pair is then folded in from LDS while those loads are in
+        // flight:
         //   S^T = K Q^T     head_dim / 32 16x16x32 MFMAs per tile; column
         //                   j of the 16 is query head j of the group (Q^T
         //                   operand zero beyond G); lane l holds tokens
@@ -768,8 +789,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         for (int t = 0; t < F::DT; t++) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = kEmptyMax, l = 0.f;  // state of column col (same in the 4 lane groups)
 
-        // staging area of this wave: K and V rows of tile 0, then of tile 1
-        uint8_t* const stage = s_raw + wave * (4 * F::TILE);
+        // staging area of this wave: the K rows of the tile being scored,
+        // then the V rows of tile 0 and of tile 1
+        uint8_t* const stage = s_raw + wave * (3 * F::TILE);
         uint32_t koff[F::KSTEP];  // K operand of k-step s: row col, chunk 4 s + g16
 #pragma unroll
         for (int s = 0; s < F::KSTEP; s++)
@@ -787,8 +809,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
         // window (all rows when the block id was outside the pool) are
         // written as zeros, so that stale pool bytes cannot enter as NaN * 0
         auto stage_put = [&](const BlockRegs<T, D, G>& br, int tau, int64_t lb, bool ok) {
-            uint8_t* kst = stage + tau * 2 * F::TILE;
-            uint8_t* vst = kst + F::TILE;
+            uint8_t* kst = stage;
+            uint8_t* vst = stage + (1 + tau) * F::TILE;
             const int64_t first = lb * kBS;
             const bool full = ok && first >= lo && first + kBS <= L;
 #pragma unroll
@@ -805,13 +827,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             }
         };
         auto stage_zero_v = [&](int tau) {  // V rows of a tile the pair does not have
-            uint8_t* vst = stage + tau * 2 * F::TILE + F::TILE;
+            uint8_t* vst = stage + (1 + tau) * F::TILE;
 #pragma unroll
             for (int c = 0; c < F::TILE / (64 * 16); c++)
                 *reinterpret_cast<u32x4*>(vst + (c * 64 + lane) * 16) = u32x4{0, 0, 0, 0};
         };
-        auto scores = [&](int tau) -> f32x4 {
-            const uint8_t* kst = stage + tau * 2 * F::TILE;
+        auto scores = [&]() -> f32x4 {  // S^T of the tile whose K rows are staged
+            const uint8_t* kst = stage;
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < F::KSTEP; k++)
@@ -819,10 +841,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             return s;
         };
         // fold the staged pair (tiles i and i + 1 of this wave) into the state
-        auto fold_pair = [&](int i, bool okA, bool okB, bool hasB) {
+        auto fold_pair = [&](int i, bool okA, bool okB, bool hasB, const f32x4& sA,
+                             const f32x4& sB) {
             const int64_t pA = (lb0 + wave + (int64_t)i * kWaves) * kBS + 4 * g16;
             const int64_t pB = pA + kWaves * kBS;
-            const f32x4 sA = scores(0), sB = scores(1);
             float sv[8];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
@@ -880,7 +902,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
 #pragma unroll
             for (int t = 0; t < F::DT; t++) {
                 const u32x2 v0 = tr_read(stage + F::TILE + voff[t]);
-                const u32x2 v1 = tr_read(stage + 3 * F::TILE + voff[t]);
+                const u32x2 v1 = tr_read(stage + 2 * F::TILE + voff[t]);
                 const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
                 for (int k = 0; k < NP; k++) oacc[t] = mfma16<T>(va, part[k], oacc[t]);
@@ -900,6 +922,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             put_new_row(bufA, lbA);
             stage_put(bufA, 0, lbA, curA);
             if (i + 2 < my_n) load_block<T, D, G>(bufA, block_ptr(i + 2, okA), vofs, g, r);
+            wave_lds_order();
+            const f32x4 sA = scores();
+            wave_lds_order();  // tile 1's K rows replace tile 0's after its scores
+            f32x4 sB = {0.f, 0.f, 0.f, 0.f};
             if (hasB) {
                 put_new_row(bufB, lbA + kWaves);
                 stage_put(bufB, 1, lbA + kWaves, curB);
@@ -908,7 +934,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeSplitArgs 
             }
             if (i + 3 < my_n) load_block<T, D, G>(bufB, block_ptr(i + 3, okB), vofs, g, r);
             wave_lds_order();
-            fold_pair(i, curA, curB, hasB);
+            if (hasB) sB = scores();
+            fold_pair(i, curA, curB, hasB, sA, sB);
         }
 
         // ---- merge the 4 wave states of the workgroup, in a fixed order ----

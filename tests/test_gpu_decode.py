@@ -217,11 +217,11 @@ def test_invalid_context_values():
     assert torch.all(torch.isnan(out[0, 2]))
 
 
-@pytest.mark.parametrize("split", [0, 1536])
+@pytest.mark.parametrize("split", [0, 2048])
 def test_single_layer_config(split):
     """1 layer, 8 KV x 3 query heads, d=128, bf16, windows of the printed
     policy's layer 0, context 32768, batch 8: every output row, at the
-    default split length and at the one the benchmark times (1536)."""
+    default split length and at the one the benchmark times (2048)."""
     say("single-layer config: fill, split", split)
     c = build_stack_case([synth.YAML_LAYER0], torch.bfloat16, 128, 3, 32768, 8, seed=102,
                          split_tokens=split)
