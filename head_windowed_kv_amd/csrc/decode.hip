@@ -21,9 +21,11 @@
 //     owns rows g, g+8 of the tile, lane r of a group 16-byte chunks r,
 //     r+8, ... of each row, so every load instruction reads whole 128-byte
 //     lines.
-// 16-bit caches (MFMA block loop): each wave writes its pair of tiles into
-// its own LDS staging area, issues the next pair's loads into the same
-// registers, and folds the pair in from LDS on the matrix cores: S^T = K Q^T
+// 16-bit caches (MFMA block loop): each wave copies the tiles of a pair into
+// its own LDS staging area (one K slot, scored before the next tile's K rows
+// replace it, and a V slot per tile), issues each tile's next load into the
+// same registers as soon as it is staged, and folds the pair in on the
+// matrix cores (three waves per SIMD up to head_dim 128): S^T = K Q^T
 // on 16x16x32 MFMAs (the 16 columns are the G query heads of the group,
 // padded), the online softmax on the S^T registers, O^T += V^T P^T with V^T
 // from transposing LDS reads (ds_read_b64_tr_b16) and P split into 16-bit
