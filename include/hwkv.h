@@ -160,9 +160,13 @@ const char *hwkv_last_error(void);
  * F16; prefill: the same block sizes and groups, BF16 or F16, head_dim 64,
  * 128 or 256).  split_tokens is the decode split length S (a multiple of
  * block_size, at most max(block_size, 2048); 0 picks the largest multiple of
- * block_size not above 1024).  On success *out owns the layout; free it with
- * hwkv_layout_destroy.  Errors: INVALID_ARG (null, n < 1, window < 1, a size
- * out of range), OVERFLOW. */
+ * block_size not above 1024).  The best S depends on the decode launch's
+ * workgroup count against the 768 an MI355X holds at once (head_dim 128);
+ * measured best: 1024 for 48 layers of one sequence at 112K and for one
+ * layer of 4 sequences at 167K, 2048 for one layer of 8 sequences at 32K,
+ * 384 for per-layer launches of one sequence.  On success *out owns the
+ * layout; free it with hwkv_layout_destroy.  Errors: INVALID_ARG (null,
+ * n < 1, window < 1, a size out of range), OVERFLOW. */
 hwkv_status hwkv_layout_create(int32_t n_layers, int32_t n_kv_heads,
                                const int32_t *windows, int32_t block_size,
                                int32_t head_dim, hwkv_dtype dtype,
