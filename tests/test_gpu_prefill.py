@@ -311,6 +311,28 @@ def test_prefill_config_161k_then_append_and_decode():
     assert worst <= DECODE_REGRESSION_TOL, worst
 
 
+def test_prefill_config_161k_head_dim256():
+    """The 161K chunk at head_dim 256 (the configuration the benchmark's
+    mixed-stack leg times: 4 sequences, 2048 rows at P = 164,864, layer-0
+    windows up to 65536, 8 KV x 3 query heads, default entry): sampled rows
+    of every head against the oracle; the bf16 output the benchmark writes
+    equals the fp32 results rounded to nearest even."""
+    P, n, G, d = synth.CTX_161K, 2048, 3, 256
+    say("prefill 161K head_dim 256: fill")
+    c = PrefillCase(list(synth.YAML_LAYER0), d, G, [P] * 4, n, seed=106)
+    say("prefill 161K head_dim 256: run")
+    out32 = c.run()
+    got = to_host_f64(out32)
+    out16 = c.run(out_dtype=torch.bfloat16)
+    assert torch.equal(out16, out32.to(torch.bfloat16))
+    del out16, out32
+    rng = np.random.default_rng(8)
+    rows = sorted(set([0, 1, 31, 32, 63, 64, 1023, 1024, 2046, 2047] +
+                      list(rng.integers(0, 2048, 10))))
+    say("prefill 161K head_dim 256: oracle on", len(rows), "rows")
+    _check(got[:, rows], c.oracle(rows=rows))
+
+
 @pytest.mark.parametrize("d,G", [(128, 3), (64, 2), (128, 8)])
 def test_f16_instances(d, G):
     """fp16 cache: fp16 MFMA tiles, P rounded once to fp16 for the PV product."""
