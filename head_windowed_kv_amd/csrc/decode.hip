@@ -549,16 +549,19 @@ void decode_split_kernel(DecodeSplitArgs a) {
     // per-lane form, one per wave in the MFMA form.  The MFMA form stages, per
     // wave, the K rows of the tile being scored and the V rows of two tiles in
     // LDS (48 KiB per workgroup at head_dim 128, so three workgroups fit a CU);
-    // the merge reuses that memory once every wave has left its loop.
+    // the workgroup merge, and in the single-launch step the merge of a head's
+    // splits, reuse that memory once every wave has left its loop.
     constexpr int SLOTS = MF ? kWaves : 2 * kWaves;
     constexpr int kAccBytes = SLOTS * G * D * 4;
     constexpr int kStageBytes = MF ? kWaves * 3 * kBS * C::ROW : 0;
+    constexpr int kMergeBytes = FUSED ? (int)sizeof(MergeLds<D, G>) : 0;
+    constexpr int kRawBytes = kAccBytes > kStageBytes ? kAccBytes : kStageBytes;
     __shared__ float s_m[kWaves][G];
     __shared__ float s_l[SLOTS][G];
     // appending modes: the new token's K and V rows, parked by the lanes of
     // the wave whose tile holds it and read back by the same lanes
     __shared__ __align__(16) uint8_t s_new[APPENDS ? 2 * C::ROW : 16];
-    __shared__ __align__(16) uint8_t s_raw[kAccBytes > kStageBytes ? kAccBytes : kStageBytes];
+    __shared__ __align__(16) uint8_t s_raw[kRawBytes > kMergeBytes ? kRawBytes : kMergeBytes];
     float(*s_acc)[G * D] = reinterpret_cast<float(*)[G * D]>(s_raw);
 
     const int lane = threadIdx.x & 63;
@@ -637,15 +640,10 @@ void decode_split_kernel(DecodeSplitArgs a) {
             const float* rec0 =
                 a.ws + ((int64_t)b * a.n_work_range + (hd.work_off - a.work_begin)) * a.rec_floats;
             // the merge's LDS: the staging / partial-state memory, which no
-            // thread reads any more, where it is large enough
-            if constexpr (sizeof(MergeLds<D, G>) <= sizeof(s_raw)) {
-                merge_in_workgroup<D, G>(*reinterpret_cast<MergeLds<D, G>*>(s_raw), rec0, (int)ns,
-                                         a.rec_floats, a.out, a.out_kind, obase);
-            } else {
-                __shared__ MergeLds<D, G> s_merge;
-                merge_in_workgroup<D, G>(s_merge, rec0, (int)ns, a.rec_floats, a.out, a.out_kind,
-                                         obase);
-            }
+            // thread reads any more
+            static_assert(sizeof(MergeLds<D, G>) <= sizeof(s_raw), "merge LDS aliases s_raw");
+            merge_in_workgroup<D, G>(*reinterpret_cast<MergeLds<D, G>*>(s_raw), rec0, (int)ns,
+                                     a.rec_floats, a.out, a.out_kind, obase);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
