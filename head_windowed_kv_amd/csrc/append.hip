@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
             // read, not written
             const int64_t first_kept = (int64_t)a.n_new - (int64_t)hd.nblocks * bs;
             auto kept = [&](int u) {
-                const int tk = tok0 + ts + u * tpp;
+                const int64_t tk = (int64_t)tok0 + ts + u * tpp;
                 return tk < tok1 && tk >= first_kept;
             };
             auto load = [&](int u, uint4& kc, uint4& vc) {
