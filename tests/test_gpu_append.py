@@ -65,6 +65,16 @@ def test_permuted_table_seq_slots_and_layer_range():
                 layer_begin=1, n_layers=2)
 
 
+def test_rows_wider_than_a_workgroup():
+    # 12 KV heads of fp32 d=128: a token row of all heads is 384 16-byte
+    # chunks, more than a workgroup's threads, so each thread walks several
+    # chunks of one token; chunks longer than some rings, wraparound
+    windows = [[16, 31, 129, 1, 64, 200, 17, 33, 1000, 2, 48, 65],
+               [7, 300, 16, 90, 1, 513, 40, 8, 65, 129, 1000, 3]]
+    script = [([0, 3], 1), ([1, 4], 70), ([71, 74], 300), ([371, 374], 1100), ([1471, 1474], 5)]
+    _run_script(windows, "f32", 128, 2, 2, script, seed=205)
+
+
 def test_f32_d128_many_sequences():
     windows = [[16, 31, 129]]
     script = [([int(x) for x in np.arange(9) * 7], 40), ([int(x) for x in np.arange(9) * 7 + 40], 1)]
